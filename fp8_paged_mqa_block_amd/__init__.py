@@ -1,0 +1,156 @@
+"""FP8 paged MQA logits + per-row top-k on MI355X (gfx950).
+
+A thin ctypes binding over ``libpmqa.so`` (C ABI in ``include/pmqa.h``).  It only
+checks and marshals arguments: every step of the computation runs in the
+library's HIP kernels.  torch tensors provide the device memory and the
+stream.  There is no fallback: when the library is missing or no GPU is
+visible the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PmqaError",
+    "load_library",
+    "library_path",
+    "paged_mqa_logits",
+    "topk_per_row",
+    "EXPORTS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libpmqa.so")
+_lib: Optional[ctypes.CDLL] = None
+
+# Every symbol include/pmqa.h declares.
+EXPORTS = ("paged_mqa_logits", "topk_per_row", "pmqa_status_string", "pmqa_version")
+
+_STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_NULL", 2: "PMQA_ERR_SHAPE", 3: "PMQA_ERR_UNSUPPORTED",
+           4: "PMQA_ERR_ALIGNMENT", 5: "PMQA_ERR_HIP"}
+
+
+class PmqaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libpmqa.so (built in-tree by fp8_paged_mqa_block_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m fp8_paged_mqa_block_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    c_i32, c_i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.paged_mqa_logits.restype = ctypes.c_int
+    lib.paged_mqa_logits.argtypes = [vp, vp, vp, vp, vp, c_i32, c_i32, vp, c_i64, c_i32, c_i32,
+                                     c_i32, c_i64, vp]
+    lib.topk_per_row.restype = ctypes.c_int
+    lib.topk_per_row.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp]
+    lib.pmqa_status_string.restype = ctypes.c_char_p
+    lib.pmqa_status_string.argtypes = [ctypes.c_int]
+    lib.pmqa_version.restype = ctypes.c_int32
+    lib.pmqa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = load_library().pmqa_status_string(status).decode()
+        raise PmqaError(fn, status, msg)
+
+
+def _stream_handle(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream)
+
+
+def _need(cond: bool, what: str) -> None:
+    if not cond:
+        raise ValueError(what)
+
+
+def _byte_view(t: torch.Tensor, name: str) -> torch.Tensor:
+    _need(t.dtype in (torch.uint8, torch.float8_e4m3fn), f"{name} must be uint8 or float8_e4m3fn, got {t.dtype}")
+    return t
+
+
+def paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
+                     context_lens: torch.Tensor, block_tables: torch.Tensor, page_size: int,
+                     next_n: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Enqueue the logits step; writes ``out`` in place and returns it.
+
+    q            [B*next_n, H, 128] or [B, next_n, H, 128], e4m3fn (or its uint8 bytes), contiguous
+    kv_cache     page pool [num_pages, page_size, 132] bytes (any contiguous shape)
+    weights      [B*next_n, H] float32, contiguous
+    context_lens [B] int32
+    block_tables [B, W] int64, contiguous (W entries per request)
+    out          [B*next_n, cols] float32, contiguous (cols = the row stride)
+    """
+    lib = load_library()
+    _byte_view(q, "q")
+    _byte_view(kv_cache, "kv_cache")
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("weights", weights),
+                    ("context_lens", context_lens), ("block_tables", block_tables), ("out", out)):
+        _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(weights.dtype == torch.float32, "weights must be float32")
+    _need(context_lens.dtype == torch.int32, "context_lens must be int32")
+    _need(block_tables.dtype == torch.int64, "block_tables must be int64 (int32 ids wrap past 2^31 bytes)")
+    _need(out.dtype == torch.float32, "out must be float32")
+    _need(q.is_contiguous() and kv_cache.is_contiguous() and weights.is_contiguous()
+          and context_lens.is_contiguous(), "q, kv_cache, weights, context_lens must be contiguous")
+    B = context_lens.shape[0]
+    _need(context_lens.dim() == 1, "context_lens must be 1-D")
+    if q.dim() == 4:
+        _need(q.shape[0] == B and q.shape[1] == next_n, "q [B, next_n, H, D] does not match")
+        q = q.reshape(B * next_n, q.shape[2], q.shape[3])
+    _need(q.dim() == 3 and q.shape[0] == B * next_n, "q must be [B*next_n, H, D]")
+    H, D = int(q.shape[1]), int(q.shape[2])
+    _need(tuple(weights.shape) == (B * next_n, H), "weights must be [B*next_n, H]")
+    # the row stride doubles as the row's capacity in the C ABI, so rows must be
+    # exactly as wide as their stride
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B and block_tables.is_contiguous(),
+          "block_tables must be a contiguous [B, W] tensor")
+    _need(out.dim() == 2 and out.shape[0] == B * next_n and out.is_contiguous(),
+          "out must be a contiguous [B*next_n, cols] tensor")
+    ts = block_tables.shape[1]
+    st = lib.paged_mqa_logits(q.data_ptr(), kv_cache.data_ptr(), weights.data_ptr(),
+                              context_lens.data_ptr(), block_tables.data_ptr(), int(page_size),
+                              int(next_n), out.data_ptr(), int(out.shape[1]), int(B), H, D,
+                              int(max(ts, 1)), _stream_handle(out, stream))
+    _check("paged_mqa_logits", st)
+    return out
+
+
+def topk_per_row(logits: torch.Tensor, context_lens: torch.Tensor, k: int, out_idx: torch.Tensor,
+                 next_n: int = 1, stream=None) -> torch.Tensor:
+    """Enqueue the per-row top-k; writes ``out_idx`` [B*next_n, k] int32 in place and returns it."""
+    lib = load_library()
+    for name, t in (("logits", logits), ("context_lens", context_lens), ("out_idx", out_idx)):
+        _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.is_contiguous(),
+          "logits must be a contiguous 2-D float32 tensor")
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1 and context_lens.is_contiguous(),
+          "context_lens must be contiguous 1-D int32")
+    B = context_lens.shape[0]
+    _need(logits.shape[0] == B * next_n, "logits must have B*next_n rows")
+    _need(out_idx.dtype == torch.int32 and out_idx.is_contiguous()
+          and tuple(out_idx.shape) == (B * next_n, k), "out_idx must be contiguous int32 [B*next_n, k]")
+    st = lib.topk_per_row(logits.data_ptr(), context_lens.data_ptr(), int(k), out_idx.data_ptr(),
+                          int(B), int(next_n), int(logits.shape[1]), _stream_handle(out_idx, stream))
+    _check("topk_per_row", st)
+    return out_idx

@@ -1,0 +1,118 @@
+// C-ABI entry points: host-side argument checks, launch geometry, status codes.
+// Declarations and the full argument contract are in include/pmqa.h.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pmqa.h"
+#include "pmqa_internal.h"
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2_exact(int64_t x) {
+  int l = 0;
+  while ((int64_t{1} << l) < x) ++l;
+  return l;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pmqa_status_string(pmqa_status status) {
+  switch (status) {
+    case PMQA_OK: return "ok";
+    case PMQA_ERR_NULL: return "null pointer argument";
+    case PMQA_ERR_SHAPE: return "size or stride out of range";
+    case PMQA_ERR_UNSUPPORTED: return "unsupported shape (num_heads must be 16/32/64/128, head_dim 128)";
+    case PMQA_ERR_ALIGNMENT: return "pointer not aligned as required";
+    case PMQA_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+int32_t pmqa_version(void) { return 100; }
+
+pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const float* weights,
+                             const int32_t* context_lens, const int64_t* block_tables,
+                             int32_t page_size, int32_t next_n, float* out,
+                             int64_t out_row_stride, int32_t batch, int32_t num_heads,
+                             int32_t head_dim, int64_t block_table_stride, void* stream) {
+  if (batch < 0 || next_n < 1 || out_row_stride < 1 || block_table_stride < 1)
+    return PMQA_ERR_SHAPE;
+  if (!(page_size == 8 || page_size == 16 || page_size == 32 || page_size == 64 ||
+        page_size == 128 || page_size == 256))
+    return PMQA_ERR_SHAPE;
+  if (head_dim != pmqa::kHeadDim) return PMQA_ERR_UNSUPPORTED;
+  if (!(num_heads == 16 || num_heads == 32 || num_heads == 64 || num_heads == 128))
+    return PMQA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
+  if (batch == 0) return PMQA_OK;
+  if (!q || !kv_cache || !weights || !context_lens || !block_tables || !out)
+    return PMQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(weights, 16) || !aligned(kv_cache, 4) || !aligned(out, 4) ||
+      !aligned(context_lens, 4) || !aligned(block_tables, 8))
+    return PMQA_ERR_ALIGNMENT;
+
+  pmqa::LogitsParams p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.kv = static_cast<const uint8_t*>(kv_cache);
+  p.w = weights;
+  p.ctx = context_lens;
+  p.tables = block_tables;
+  p.out = out;
+  p.out_stride = out_row_stride;
+  p.table_stride = block_table_stride;
+  p.page_bytes = (int64_t)page_size * pmqa::kRecordBytes;
+  p.batch = batch;
+  p.next_n = next_n;
+  p.page_size = page_size;
+  p.log2_page = log2_exact(page_size);
+  // the grid covers every token a request could have: the table row's capacity
+  // and the output row's width bound it
+  int64_t max_tokens = block_table_stride * (int64_t)page_size;
+  if (out_row_stride < max_tokens) max_tokens = out_row_stride;
+  if (max_tokens > INT32_MAX) max_tokens = INT32_MAX;
+  p.max_tokens = (int32_t)max_tokens;
+  const int wave_tokens = pmqa::logits_wave_tokens();
+  const int64_t n_chunks = (max_tokens + wave_tokens - 1) / wave_tokens;
+  const int jw = pmqa::logits_rows_per_wave(num_heads, next_n);
+  const int64_t n_rgroups = (next_n + jw - 1) / jw;
+  const int64_t n_units = (int64_t)batch * n_chunks * n_rgroups;
+  if (n_units > (int64_t)UINT32_MAX / 2) return PMQA_ERR_SHAPE;
+  p.n_chunks = (int32_t)n_chunks;
+  p.n_rgroups = (int32_t)n_rgroups;
+  p.n_units = (uint32_t)n_units;
+  if (!is_pow2(page_size)) return PMQA_ERR_SHAPE;
+
+  hipError_t e = pmqa::launch_logits(p, num_heads, jw, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
+}
+
+pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,
+                         int32_t* out_idx, int32_t batch, int32_t next_n,
+                         int64_t logits_row_stride, void* stream) {
+  if (batch < 0 || next_n < 1 || logits_row_stride < 1) return PMQA_ERR_SHAPE;
+  if (k < 1 || k > 2048) return PMQA_ERR_SHAPE;
+  if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
+  if (batch == 0) return PMQA_OK;
+  if (!logits || !context_lens || !out_idx) return PMQA_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(context_lens, 4) || !aligned(out_idx, 4))
+    return PMQA_ERR_ALIGNMENT;
+  pmqa::TopkParams p{};
+  p.logits = logits;
+  p.ctx = context_lens;
+  p.out_idx = out_idx;
+  p.row_stride = logits_row_stride;
+  p.batch = batch;
+  p.next_n = next_n;
+  p.k = k;
+  hipError_t e = pmqa::launch_topk(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+/*
+ * pmqa.h - C ABI of the MI355X (gfx950) FP8 paged MQA logits + per-row top-k library.
+ *
+ * The two operations are the sparse-attention indexer's decode scoring step and
+ * the selection that follows it:
+ *
+ *   paged_mqa_logits : the op the pages call deepgemm_fp8_paged_mqa_logits
+ *                      (aiter PR #4244 "fix silent tail-row drop in
+ *                      deepgemm_fp8_paged_mqa_logits at large output stride":
+ *                      bug description, root cause and fix; the reproducer
+ *                      gives its tensors and their shapes).
+ *   topk_per_row     : the follow-on top_k_per_row_decode that turns each logits
+ *                      row into the sparse-KV index list (same page, first
+ *                      paragraph).
+ *
+ * Score (the DSA indexer score; the pages name the op but print no formula, so
+ * this is the reading adopted): for output row r = b*next_n + j and token t,
+ *
+ *     logit[r, t] = sum_h  w[r, h] * relu( scale_t * sum_d q[r, h, d] * k_t[d] )
+ *
+ * with q and k in OCP e4m3fn and the product accumulated in fp32 on the fp8
+ * matrix cores.  Causal mask (reading adopted for MTP): the next_n rows of a
+ * request are its last next_n positions, so row j sees
+ * visible = clamp(ctx_b - next_n + j + 1, 0, ctx_b) tokens; columns
+ * [visible, ctx_b) receive -inf and columns >= ctx_b are never written.
+ *
+ * Conventions shared by every entry point:
+ *   - every pointer argument is DEVICE memory owned by the caller; the library
+ *     allocates nothing and keeps no state besides a per-device cache of the
+ *     compute-unit count;
+ *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising; results are ordered only with
+ *     later work on the same stream;
+ *   - arguments checkable on the host are checked BEFORE anything is enqueued:
+ *     on any error nothing is launched and a non-zero pmqa_status is returned.
+ *     Nothing is silently dropped or truncated on the host side;
+ *   - integer sizes are element counts unless the name says bytes.
+ */
+#ifndef PMQA_H_
+#define PMQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PMQA_OK = 0,
+  PMQA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  PMQA_ERR_SHAPE = 2,       /* a size or stride is out of range                  */
+  PMQA_ERR_UNSUPPORTED = 3, /* a valid but unimplemented shape (heads, head_dim) */
+  PMQA_ERR_ALIGNMENT = 4,   /* a pointer lacks the alignment stated below        */
+  PMQA_ERR_HIP = 5          /* the HIP runtime reported an error at launch       */
+} pmqa_status;
+
+/*
+ * paged_mqa_logits - FP8 paged MQA logits over each request's paged K cache.
+ *
+ * q             [batch*next_n, num_heads, head_dim] e4m3fn bytes, row-major,
+ *               16-byte aligned.  Row r = b*next_n + j (the pages' q is
+ *               [B, next_n, H, D]).
+ * kv_cache      the page pool, [num_pages, page_size, head_dim + 4] bytes,
+ *               4-byte aligned.  Token s of page p is the record starting at
+ *               byte (p*page_size + s)*(head_dim+4): head_dim e4m3fn codes then
+ *               the token's fp32 scale, little endian (the pages' cache is
+ *               [num_blocks, block_size, 1, D+4] fp8 whose last 4 bytes per
+ *               token are viewed as one fp32 scale).  Byte offsets are formed in
+ *               64-bit, so pools larger than 2^31 / 2^32 bytes are addressed
+ *               correctly (ATOM PR #2533 "Address Triton decode KV rows with
+ *               int64 ids").
+ * weights       [batch*next_n, num_heads] fp32, 16-byte aligned.
+ * context_lens  [batch] int32, ctx_b >= 0 (negative values count as 0).
+ * block_tables  [batch, block_table_stride] int64 page ids.  Only the first
+ *               ceil(ctx_b/page_size) entries of row b are read; the rest may
+ *               hold anything.  Preconditions not checked on the host (they
+ *               live in device memory): read ids lie in [0, num_pages).
+ * page_size     tokens per page: 8, 16, 32, 64, 128 or 256.  Pages smaller than
+ *               the 16-token matrix tile are assembled into one tile (aiter
+ *               PR #6626 section 1: a tile is built from several 8-token pages).
+ * next_n        MTP query positions per request, >= 1.
+ * out           fp32 logits; row r starts at element r*out_row_stride (the row
+ *               offset is computed in 64-bit: rows whose byte offset passes
+ *               2^31 are written, aiter PR #4244 "Fix").  4-byte aligned.
+ *               Columns [0, visible) get scores, [visible, ctx_eff) get -inf,
+ *               nothing else is written (ctx_eff defined below).
+ * out_row_stride  elements between output rows, >= 1.
+ * batch         number of requests, >= 0 (0 enqueues nothing).
+ * num_heads     16, 32, 64 or 128.
+ * head_dim      128.
+ * block_table_stride  entries between block-table rows, >= 1.
+ * stream        hipStream_t to enqueue on.
+ *
+ * ctx_eff = min(ctx_b, block_table_stride*page_size, out_row_stride): the
+ * kernel never reads past a table row nor writes past an output row, even
+ * when the caller's context length exceeds them (a precondition violation).
+ */
+pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const float* weights,
+                             const int32_t* context_lens, const int64_t* block_tables,
+                             int32_t page_size, int32_t next_n, float* out,
+                             int64_t out_row_stride, int32_t batch, int32_t num_heads,
+                             int32_t head_dim, int64_t block_table_stride, void* stream);
+
+/*
+ * topk_per_row - indices of the k largest logits of each row (the follow-on
+ * top_k_per_row_decode of aiter PR #4244, first paragraph).
+ *
+ * logits        fp32, row r at element r*logits_row_stride, 4-byte aligned.
+ *               Read only on [0, visible(r)) with visible as for
+ *               paged_mqa_logits (clamped to logits_row_stride).
+ * context_lens  [batch] int32, as for paged_mqa_logits.
+ * k             1 .. 2048.
+ * out_idx       [batch*next_n, k] int32, row-major.  Row r receives the
+ *               min(k, visible(r)) token indices of its largest scores, in
+ *               unspecified order, and -1 in the remaining slots.  Every row
+ *               is written, including rows with nothing visible.  Among equal
+ *               scores at the k-th boundary the lowest indices are taken.
+ * batch, next_n as for paged_mqa_logits.
+ * logits_row_stride  elements between logits rows, >= 1.
+ * stream        hipStream_t to enqueue on.
+ */
+pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,
+                         int32_t* out_idx, int32_t batch, int32_t next_n,
+                         int64_t logits_row_stride, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* pmqa_status_string(pmqa_status status);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int32_t pmqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMQA_H_ */

@@ -1,0 +1,100 @@
+"""The C-ABI library on the host (CPU only, no GPU needed).
+
+Loads libpmqa.so, checks that every symbol include/pmqa.h declares is exported,
+and drives the host-side argument checks: each invalid argument returns its
+status code before anything is enqueued (so these calls never touch a GPU).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_paged_mqa_block_amd as pm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP = range(6)
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "pmqa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(\w+)\s*\(", text, flags=re.M)) - {"if"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pm.library_path()):
+        pytest.fail("libpmqa.so not built: run python -m fp8_paged_mqa_block_amd.build")
+    return pm.load_library()
+
+
+def test_header_declares_the_exports():
+    assert header_symbols() == sorted(pm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pm.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for sym in header_symbols():
+        assert sym in exported, sym
+        assert hasattr(lib, sym)
+
+
+def test_status_strings_and_version(lib):
+    for s in range(6):
+        assert lib.pmqa_status_string(s)
+    assert lib.pmqa_status_string(99) == b"unknown status"
+    assert lib.pmqa_version() >= 100
+
+
+# A fake, suitably aligned "device" address: the checks below all fail before
+# the library could dereference or launch anything.
+P = 0x10000
+
+
+def logits(lib, **kw):
+    a = dict(q=P, kv=P, w=P, ctx=P, tab=P, ps=64, nn=1, out=P, ors=1024, b=2, h=64, d=128,
+             ts=16, stream=None)
+    a.update(kw)
+    return lib.paged_mqa_logits(a["q"], a["kv"], a["w"], a["ctx"], a["tab"], a["ps"], a["nn"],
+                                a["out"], a["ors"], a["b"], a["h"], a["d"], a["ts"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ERR_NULL), (dict(kv=None), ERR_NULL), (dict(w=None), ERR_NULL),
+    (dict(ctx=None), ERR_NULL), (dict(tab=None), ERR_NULL), (dict(out=None), ERR_NULL),
+    (dict(nn=0), ERR_SHAPE), (dict(b=-1), ERR_SHAPE), (dict(ors=0), ERR_SHAPE),
+    (dict(ts=0), ERR_SHAPE), (dict(ps=4), ERR_SHAPE), (dict(ps=24), ERR_SHAPE),
+    (dict(ps=512), ERR_SHAPE), (dict(d=64), ERR_UNSUPPORTED), (dict(h=48), ERR_UNSUPPORTED),
+    (dict(h=256), ERR_UNSUPPORTED), (dict(q=P + 8), ERR_ALIGN), (dict(w=P + 4), ERR_ALIGN),
+    (dict(kv=P + 2), ERR_ALIGN), (dict(out=P + 2), ERR_ALIGN), (dict(tab=P + 4), ERR_ALIGN),
+    (dict(b=0, q=None, kv=None), OK),
+])
+def test_logits_host_checks(lib, kw, status):
+    assert logits(lib, **kw) == status
+
+
+def topk(lib, **kw):
+    a = dict(lg=P, ctx=P, k=2048, out=P, b=4, nn=1, rs=8192, stream=None)
+    a.update(kw)
+    return lib.topk_per_row(a["lg"], a["ctx"], a["k"], a["out"], a["b"], a["nn"], a["rs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lg=None), ERR_NULL), (dict(ctx=None), ERR_NULL), (dict(out=None), ERR_NULL),
+    (dict(k=0), ERR_SHAPE), (dict(k=2049), ERR_SHAPE), (dict(nn=0), ERR_SHAPE),
+    (dict(rs=0), ERR_SHAPE), (dict(b=-3), ERR_SHAPE), (dict(lg=P + 2), ERR_ALIGN),
+    (dict(out=P + 1), ERR_ALIGN), (dict(b=0, lg=None), OK),
+])
+def test_topk_host_checks(lib, kw, status):
+    assert topk(lib, **kw) == status
+
+
+def test_binding_rejects_wrong_dtypes_before_the_library():
+    import torch
+    t = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        pm.paged_mqa_logits(t, t, t, t, t, 64, 1, t)

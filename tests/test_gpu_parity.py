@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases are compared element by element on every row (several 16-token
+tiles, 64-token iterations and 256-token wave units, with ragged tails, every
+page size, head count and next_n class, zero contexts).  The five workloads run
+at full size in the launch configuration the benchmark times; their rows are
+checked on sampled requests (the oracle computes them one by one), plus
+properties that hold at any size: full-row coverage of the [1024, 1<<20]
+output, no write past a context, bit-identical results across compact and
+padded tables, output strides, batch splits, table permutations and repeat
+runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.parity import (SENTINEL_BITS, check_rows, check_topk, check_untouched_rows,
+                          new_out, oracle_rows, run_logits, say, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def topk_gpu(pm, wl, out, k=None, ctx=None):
+    k = k or wl.topk
+    idx = torch.full((wl.rows, k), -7, dtype=torch.int32, device="cuda")
+    say(f"[gpu] topk_per_row {wl.name} rows={wl.rows} k={k} stride={out.shape[1]}")
+    pm.topk_per_row(out, ctx, k, idx, next_n=wl.next_n)
+    torch.cuda.synchronize()
+    return idx
+
+
+SMALL = [
+    dict(batch=3, next_n=1, heads=64, page_size=64, ctx_range=(1, 700)),
+    dict(batch=4, next_n=2, heads=128, page_size=256, ctx_range=(2, 1500)),
+    dict(batch=6, next_n=3, heads=64, page_size=8, ctx_range=(0, 900), zero_every=3),
+    dict(batch=5, next_n=4, heads=32, page_size=16, ctx_range=(0, 600)),
+    dict(batch=5, next_n=1, heads=16, page_size=32, ctx_range=(1, 520)),
+    dict(batch=4, next_n=2, heads=64, page_size=128, ctx_range=(100, 1100)),
+    dict(batch=3, next_n=5, heads=64, page_size=64, ctx_range=(0, 400)),
+    dict(batch=3, next_n=3, heads=128, page_size=8, ctx_range=(1, 300)),
+    dict(batch=4, next_n=4, heads=16, page_size=256, ctx_range=(0, 800)),
+    dict(batch=2, next_n=1, heads=64, page_size=16,
+         context_lens=[1, 15]),
+    dict(batch=7, next_n=2, heads=32, page_size=8,
+         context_lens=[0, 1, 2, 16, 17, 255, 257]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_cases_every_row(gpu_lib, case):
+    kw = dict(SMALL[case])
+    for seed in (0, 1):
+        wl = synth.build_workload(f"small{case}", head_dim=128, table="permuted", topk=64,
+                                  seed=seed, **kw)
+        wl.out_row_stride = int(max(1, wl.context_lens.max())) + 37
+        d = upload(wl)
+        out = run_logits(gpu_lib, wl, d, label=f"seed={seed}")
+        ref = oracle_rows(wl)
+        check_rows(wl, out, ref)
+        for k in (1, 16, 64):
+            idx = topk_gpu(gpu_lib, wl, out, k=k, ctx=d["ctx"])
+            check_topk(idx, ref, k)
+
+
+def test_config1_tiny_decode(gpu_lib):
+    wl = synth.make_config(1)
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d)
+    ref = oracle_rows(wl)
+    worst = check_rows(wl, out, ref)
+    say(f"config1 worst rel err {worst:.3e}")
+    idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+    check_topk(idx, ref, wl.topk)
+
+
+@pytest.fixture(scope="module")
+def cfg2():
+    return synth.make_config(2)
+
+
+def test_config2_decode_all_rows(gpu_lib, cfg2):
+    wl = cfg2
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d)
+    ref = oracle_rows(wl)
+    worst = check_rows(wl, out, ref)
+    say(f"config2 worst rel err {worst:.3e}")
+    idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+    check_topk(idx, ref, wl.topk)
+
+
+def test_invariants_bit_identical(gpu_lib, cfg2):
+    """Strides, batch split, table permutation and repeat runs change nothing."""
+    wl = cfg2
+    d = upload(wl)
+    a = run_logits(gpu_lib, wl, d, label="ref")
+    b = run_logits(gpu_lib, wl, d, label="repeat")
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    wide = run_logits(gpu_lib, wl, d, stride=wl.out_row_stride + 4099, label="wide")
+    assert torch.equal(a.view(torch.int32), wide[:, : wl.out_row_stride].view(torch.int32))
+    assert bool((wide[:, wl.out_row_stride:].view(torch.int32) == SENTINEL_BITS).all())
+    # batch split: two launches over the halves
+    h = wl.batch // 2
+    for lo, hi in ((0, h), (h, wl.batch)):
+        part = new_out((hi - lo) * wl.next_n, wl.out_row_stride)
+        say(f"[gpu] paged_mqa_logits batch split [{lo},{hi})")
+        nn = wl.next_n
+        gpu_lib.paged_mqa_logits(d["q"][lo * nn:hi * nn], d["kv"], d["w"][lo * nn:hi * nn],
+                                 d["ctx"][lo:hi].contiguous(), d["tab"][lo:hi].contiguous(),
+                                 wl.page_size, nn, part)
+        torch.cuda.synchronize()
+        assert torch.equal(part.view(torch.int32), a[lo * nn:hi * nn].view(torch.int32))
+    # identity table over a re-laid pool holding the same pages
+    ps, W = wl.page_size, wl.block_tables.shape[1]
+    npg = (wl.context_lens.astype(np.int64) + ps - 1) // ps
+    rec = ps * (wl.head_dim + 4)
+    src = wl.kv_cache.reshape(-1, rec)
+    pool = np.zeros(((wl.batch * W) + 1, rec), dtype=np.uint8)
+    tab = np.full((wl.batch, W), wl.batch * W, dtype=np.int64)
+    for r in range(wl.batch):
+        for i in range(int(npg[r])):
+            pool[r * W + i] = src[wl.block_tables[r, i]]
+            tab[r, i] = r * W + i
+    d2 = dict(d)
+    d2["kv"] = torch.from_numpy(pool.reshape(-1)).cuda()
+    d2["tab"] = torch.from_numpy(tab).cuda()
+    c = run_logits(gpu_lib, wl, d2, label="identity-table")
+    assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+
+
+@pytest.fixture(scope="module")
+def cfg3():
+    return synth.make_config(3)
+
+
+def test_config3_wide_output_rows_past_2gib(gpu_lib, cfg3):
+    wl = cfg3
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d)  # [1024, 1<<20] fp32: rows >= 512 start past 2^31 bytes
+    # every row is touched, nothing is written past a context (checked on the GPU)
+    bits = out.view(torch.int32)
+    ctx_rows = d["ctx"].repeat_interleave(wl.next_n)
+    cols = torch.arange(out.shape[1], device="cuda")
+    for r0 in range(0, wl.rows, 64):
+        blk = bits[r0 : r0 + 64]
+        untouched = (blk == SENTINEL_BITS)
+        assert bool((~untouched).any(dim=1).all()), f"untouched row in [{r0}, {r0 + 64})"
+        past = cols[None, :] >= ctx_rows[r0 : r0 + 64, None]
+        assert not bool((past & ~untouched).any()), f"write past a context in [{r0}, {r0 + 64})"
+    # sampled requests vs the oracle: both sides of the 2^31-byte boundary
+    rng = np.random.default_rng(0)
+    reqs = sorted(set([0, 127, 128, 255] + rng.choice(wl.batch, 4, replace=False).tolist()))
+    ref = oracle_rows(wl, requests=reqs)
+    worst = check_rows(wl, out, ref, requests=reqs)
+    say(f"config3 sampled worst rel err {worst:.3e}")
+    idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+    rows = [r for b in reqs for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
+    check_topk(idx, ref, wl.topk, rows=rows)
+
+
+@pytest.fixture(scope="module")
+def cfg4():
+    return synth.make_config(4)
+
+
+def test_config4_small_pages_compact_and_padded(gpu_lib, cfg4):
+    wl = cfg4
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d, label="compact")
+    dp = dict(d)
+    dp["tab"] = torch.from_numpy(wl.extra_tables["padded"]).cuda()
+    outp = run_logits(gpu_lib, wl, dp, label="padded")
+    assert torch.equal(out.view(torch.int32), outp.view(torch.int32))
+    boundary = -(-(2 ** 31) // (wl.page_size * (wl.head_dim + 4)))
+    npg = (wl.context_lens.astype(np.int64) + 7) // 8
+    high = [b for b in range(wl.batch) if (wl.block_tables[b, : npg[b]] >= boundary).any()]
+    assert high
+    zero = [b for b in range(wl.batch) if wl.context_lens[b] == 0]
+    reqs = sorted(set([1, 2, 3, 4, 5] + high[:3]) - set(zero))
+    ref = oracle_rows(wl, requests=reqs)
+    worst = check_rows(wl, out, ref, requests=reqs)
+    check_untouched_rows(wl, out, zero)
+    say(f"config4 sampled worst rel err {worst:.3e}")
+    idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+    rows = [r for b in reqs for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
+    check_topk(idx, ref, wl.topk, rows=rows)
+    zrows = [r for b in zero for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
+    assert bool((idx[zrows] == -1).all())
+
+
+def test_config5_long_context(gpu_lib):
+    wl = synth.make_config(5)
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d)
+    reqs = [0, 13, 31]
+    ref = oracle_rows(wl, requests=reqs)
+    worst = check_rows(wl, out, ref, requests=reqs)
+    say(f"config5 sampled worst rel err {worst:.3e}")
+    idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+    rows = [r for b in reqs for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
+    check_topk(idx, ref, wl.topk, rows=rows)
+
+
+@pytest.mark.parametrize("ties", [0, 3])
+def test_topk_synthetic_rows(gpu_lib, ties):
+    """The top-k alone on seeded score rows: exact sets (same fp32 inputs on both
+    sides), lowest indices among equal scores, every row length class."""
+    lens = [0, 1, 100, 2047, 2048, 2049, 4000, 16384, 16385, 40000, 131072]
+    width = max(lens)
+    dense = synth.make_logit_rows(len(lens), width, lens, seed=5, ties=ties)
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    logits = torch.from_numpy(dense).cuda()
+    for k in (1, 7, 2048):
+        idx = torch.full((len(lens), k), -7, dtype=torch.int32, device="cuda")
+        say(f"[gpu] topk_per_row synthetic ties={ties} k={k}")
+        gpu_lib.topk_per_row(logits, ctx, k, idx, next_n=1)
+        torch.cuda.synchronize()
+        want = oracle.topk_per_row([dense[r, :n] for r, n in enumerate(lens)], k)
+        got = idx.cpu().numpy()
+        for r, n in enumerate(lens):
+            m = min(k, n)
+            assert sorted(got[r, :m].tolist()) == sorted(want[r, :m].tolist()), f"row {r} n={n} k={k}"
+            assert np.all(got[r, m:] == -1)
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+def test_short_rows_meet_row_tolerance(gpu_lib, heads):
+    """Rows that see only a few tokens, with sign-cancelling weights: the row's
+    largest score can be small next to its terms, which is where an inexact sum
+    of products would show."""
+    lens = [1, 2, 3, 4, 5, 8, 16, 127, 128, 129, 130, 131] * 40
+    wl = synth.build_workload("short", batch=len(lens), next_n=2, heads=heads, head_dim=128,
+                              page_size=16, context_lens=lens, table="permuted", topk=4,
+                              seed=heads)
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d)
+    worst = check_rows(wl, out, oracle_rows(wl))
+    say(f"short rows H={heads}: worst rel err {worst:.3e}")
