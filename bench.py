@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 paged MQA logits + per-row top-k step on one MI355X.
+
+One step = paged_mqa_logits then topk_per_row over one batch of the decode
+workload (B=64 requests, next_n=1, H=64, D=128, 64-token pages, context
+lengths U[1,8192], a randomly permuted 10,000-page pool, top-k 2048).  Inputs
+are synthetic and seeded, resident in HBM before timing starts.  Sixteen
+copies of the inputs and outputs are rotated so that consecutive steps never
+find their K pages in the 256 MB last-level cache.
+
+Prints one JSON line.  `value` is context tokens scored per second over the
+whole step; `roofline` describes the logits kernel (HBM-bound at this shape),
+timed by HIP events that each of its dispatches records at kernel start and
+end in the timed region;
+`cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "context tokens scored/s (TFLOP/s fp8) + % MFMA/HBM roofline, 1×MI355X"
+HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+N_SETS = 16
+KERNEL_SOURCES = ["fp8_paged_mqa_block_amd/csrc/logits_gfx950.hip",
+                  "fp8_paged_mqa_block_amd/csrc/pmqa_host.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "logits_decode_b64_traffic.md")
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded (ctypes)."""
+
+    def __init__(self):
+        import ctypes
+
+        self.ct = ctypes
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        h = self.ct.c_void_p()
+        assert self.rt.hipEventCreate(self.ct.byref(h)) == 0
+        return h.value
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        assert self.rt.hipEventElapsedTime(self.ct.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, h):
+        self.rt.hipEventDestroy(h)
+
+
+def kernel_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl):
+    """Bytes the logits step must move: every K record of every context token,
+    one table entry per page, the fp32 outputs on [0, ctx) of every row, and
+    each row's q and weights."""
+    ctx = wl.context_lens.astype(int)
+    pages = sum((c + wl.page_size - 1) // wl.page_size for c in ctx)
+    k_bytes = int(ctx.sum()) * (wl.head_dim + 4)
+    out_bytes = int(ctx.sum()) * 4 * wl.next_n
+    table_bytes = pages * 8
+    row_bytes = wl.rows * (wl.heads * wl.head_dim + 4 * wl.heads) + 4 * wl.batch
+    return k_bytes + out_bytes + table_bytes + row_bytes
+
+
+def topk_bytes(wl):
+    vis = wl.visible_lens()
+    return int(vis.sum()) * 4 + wl.rows * wl.topk * 4 + 4 * wl.batch
+
+
+def read_traffic(digest):
+    """HBM bytes per logits launch from the committed rocprofv3 counter runs,
+    or None when the kernel sources changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_digest:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != digest:
+        return None
+    return float(t.group(1))
+
+
+def pm_rows_per_wave(wl):
+    cap = 1 if wl.heads >= 128 else (3 if wl.heads >= 64 else 4)
+    return min(wl.next_n, cap)
+
+
+def cpu_baseline(wl, min_seconds=10.0, max_reps=400):
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        rows = oracle.paged_mqa_logits(wl.q, wl.kv_cache, wl.weights, wl.context_lens,
+                                       wl.block_tables, wl.page_size, wl.next_n)
+        oracle.topk_per_row(rows, wl.topk)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    return {
+        "value": wl.scored_tokens() * reps / el,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"the whole {wl.name} workload (logits + top-k, {wl.scored_tokens()} scored tokens) "
+                  f"run {reps}x in {el:.1f} s, numpy fp64 on {threads} BLAS threads",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload number (2 = decode B=64)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=N_SETS)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path runs on a single MI355X; --gpus {args.gpus} "
+              "is not supported (requests shard by request across GPUs with no exchange, "
+              "so N GPUs run N independent copies of this step)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_paged_mqa_block_amd as pm
+    import synth
+
+    lib = pm.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    wl = synth.make_config(args.config)
+    rows, stride, k = wl.rows, wl.out_row_stride, wl.topk
+    print(f"[bench] workload {wl.name}: B={wl.batch} next_n={wl.next_n} H={wl.heads} "
+          f"ps={wl.page_size} scored={wl.scored_tokens()} sets={args.sets}", file=sys.stderr,
+          flush=True)
+
+    sets = []
+    q = torch.from_numpy(wl.q).to(dev)
+    w = torch.from_numpy(wl.weights).to(dev)
+    ctx = torch.from_numpy(wl.context_lens).to(dev)
+    tab = torch.from_numpy(wl.block_tables).to(dev)
+    kv0 = torch.from_numpy(wl.kv_cache).to(dev)
+    for s in range(args.sets):
+        kv = kv0 if s == 0 else kv0.clone()
+        out = torch.empty((rows, stride), dtype=torch.float32, device=dev)
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+        sets.append(dict(q=q.clone(), w=w.clone(), ctx=ctx.clone(), tab=tab.clone(), kv=kv,
+                         out=out, idx=idx))
+    # check once through the binding, then launch through the raw C ABI in the loop
+    pm.paged_mqa_logits(sets[0]["q"].view(torch.float8_e4m3fn), sets[0]["kv"], sets[0]["w"],
+                        sets[0]["ctx"], sets[0]["tab"], wl.page_size, wl.next_n, sets[0]["out"])
+    pm.topk_per_row(sets[0]["out"], sets[0]["ctx"], k, sets[0]["idx"], next_n=wl.next_n)
+    torch.cuda.synchronize()
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] calibration copies: 3 x {args.calibrate_copy_mib} MiB", file=sys.stderr,
+              flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+    W = wl.block_tables.shape[1]
+    largs = [(d["q"].data_ptr(), d["kv"].data_ptr(), d["w"].data_ptr(), d["ctx"].data_ptr(),
+              d["tab"].data_ptr(), wl.page_size, wl.next_n, d["out"].data_ptr(), stride,
+              wl.batch, wl.heads, wl.head_dim, W, sh) for d in sets]
+    targs = [(d["out"].data_ptr(), d["ctx"].data_ptr(), k, d["idx"].data_ptr(), wl.batch,
+              wl.next_n, stride, sh) for d in sets]
+    logits_fn, topk_fn = lib.paged_mqa_logits_timed, lib.topk_per_row_timed
+    hip = HipEvents()
+
+    def step(i, ev):
+        st = logits_fn(*largs[i % len(largs)], ev[0], ev[1])
+        st |= topk_fn(*targs[i % len(targs)], ev[2], ev[3])
+        return st
+
+    spare = [hip.create() for _ in range(4)]
+    for i in range(args.warmup):
+        assert step(i, spare) == 0
+    torch.cuda.synchronize()
+
+    # kernel start/end events recorded by the dispatches themselves
+    events = [[hip.create() for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    bad = 0
+    for i in range(args.steps):
+        bad |= step(i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert bad == 0
+    elapsed = t1 - t0
+    logits_ms = [hip.elapsed_ms(e[0], e[1]) for e in events]
+    topk_ms = [hip.elapsed_ms(e[2], e[3]) for e in events]
+    step_ms = elapsed * 1e3 / args.steps
+    for e in events + [spare]:
+        for h in e:
+            hip.destroy(h)
+
+    scored = wl.scored_tokens()
+    flops = 2.0 * wl.heads * wl.head_dim * scored
+    value = scored * args.steps / elapsed
+    lg_avg_s = float(np.mean(logits_ms)) * 1e-3
+    abytes = algorithmic_bytes(wl)
+    achieved = abytes / lg_avg_s / 1e9
+    digest = kernel_digest()
+    traffic = read_traffic(digest)
+
+    ai = flops / abytes
+    if ai > FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        roof = {"bound": "mfma", "achieved": flops / lg_avg_s / 1e12, "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof.update({
+        "traffic": traffic,
+        "kernel": f"logits_kernel<{wl.heads},{pm_rows_per_wave(wl)}>",
+        "algorithmic_bytes_per_launch": abytes,
+        "algorithmic_flops_per_launch": flops,
+        "hbm_GBps": achieved,
+        "hbm_frac": achieved / HBM_PEAK_GBPS,
+        "mfma_frac": flops / lg_avg_s / 1e12 / FP8_PEAK_TFLOPS,
+        "kernel_digest": digest,
+    })
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "next_n": wl.next_n,
+                   "heads": wl.heads, "head_dim": wl.head_dim, "page_size": wl.page_size,
+                   "context_lens": "U[1,8192]" if args.config == 2 else "see workload",
+                   "topk": k, "scored_tokens_per_step": scored, "rotated_input_sets": args.sets},
+        "tflops": flops * args.steps / elapsed / 1e12,
+        "logits_us": {"mean": lg_avg_s * 1e6, "median": float(np.median(logits_ms)) * 1e3},
+        "topk_us": {"mean": float(np.mean(topk_ms)) * 1e3, "median": float(np.median(topk_ms)) * 1e3},
+        "logits_tflops": flops / lg_avg_s / 1e12,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res, default=lambda o: o.item() if hasattr(o, "item") else str(o)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,7 +28,8 @@ _LIB_PATH = os.path.join(_PKG, "libpmqa.so")
 _lib: Optional[ctypes.CDLL] = None
 
 # Every symbol include/pmqa.h declares.
-EXPORTS = ("paged_mqa_logits", "topk_per_row", "pmqa_status_string", "pmqa_version")
+EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "topk_per_row", "topk_per_row_timed",
+           "pmqa_status_string", "pmqa_version")
 
 _STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_NULL", 2: "PMQA_ERR_SHAPE", 3: "PMQA_ERR_UNSUPPORTED",
            4: "PMQA_ERR_ALIGNMENT", 5: "PMQA_ERR_HIP"}
@@ -57,8 +58,12 @@ def load_library() -> ctypes.CDLL:
     lib.paged_mqa_logits.restype = ctypes.c_int
     lib.paged_mqa_logits.argtypes = [vp, vp, vp, vp, vp, c_i32, c_i32, vp, c_i64, c_i32, c_i32,
                                      c_i32, c_i64, vp]
+    lib.paged_mqa_logits_timed.restype = ctypes.c_int
+    lib.paged_mqa_logits_timed.argtypes = lib.paged_mqa_logits.argtypes + [vp, vp]
     lib.topk_per_row.restype = ctypes.c_int
     lib.topk_per_row.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp]
+    lib.topk_per_row_timed.restype = ctypes.c_int
+    lib.topk_per_row_timed.argtypes = lib.topk_per_row.argtypes + [vp, vp]
     lib.pmqa_status_string.restype = ctypes.c_char_p
     lib.pmqa_status_string.argtypes = [ctypes.c_int]
     lib.pmqa_version.restype = ctypes.c_int32

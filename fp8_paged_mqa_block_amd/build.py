@@ -19,6 +19,7 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
+    "-fvisibility=hidden",  # only the C ABI (PMQA_API) is exported
     # packed fp32 VALU forms stay off: the compiler may not form v_pk_*_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",

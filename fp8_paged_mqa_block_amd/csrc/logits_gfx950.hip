@@ -12,27 +12,42 @@
 // silent.
 //
 // Mapping onto CDNA4:
-//  * one wavefront owns a "wave unit": request b, a 256-token chunk of its
-//    context, and a group of up to JW of its next_n rows.  The unit's rows of
-//    q (JW*H x 128 e4m3fn) stay in VGPRs as MFMA A operands, heads on the M
-//    dimension, so each lane ends up holding 4 heads of one token and the head
-//    reduction is in-lane FMAs plus two cross-lane adds;
-//  * K is gathered straight from the paged pool into B-operand registers: lane
-//    l reads 32 bytes of token (l % 16).  Each lane forms its own token's
-//    address from the block table, so a 16-token tile may draw on several
-//    pages smaller than the tile (aiter PR #6626 section 1 builds one tile from
-//    several 8-token pages); the unit's page ids are read once, before its
-//    tiles, one id per lane, and passed to the token lanes by a lane shuffle;
+//  * the work is the list of (request, 64-token iteration) pairs over every
+//    context.  A persistent grid of waves splits that list evenly: each wave
+//    scans the context lengths on the device (the host never reads them),
+//    takes a contiguous run of iterations and walks it, so no wave is launched
+//    for an empty chunk and a long context is spread over many waves;
+//  * a wave also owns a group of up to JW of the next_n rows.  Their q (JW*H x
+//    128 e4m3fn) stays in VGPRs as MFMA A operands, loaded once per request the
+//    wave visits, heads on the M dimension, so each lane ends up holding 4
+//    heads of one token and the head reduction is in-lane FMAs plus two
+//    cross-lane adds;
+//  * K values are staged through LDS by the memory pipeline itself
+//    (global_load_lds_dwordx4): each instruction moves 8 whole token records'
+//    128 value bytes, 16 contiguous bytes per lane, so every load touches only
+//    the cache lines it uses, and no VGPR holds data in flight.  Every wave
+//    keeps a ring of 4 iterations (32 KiB) in flight.  A 16-byte chunk c of
+//    local token t lands at t*128 + 16*(c ^ (t & 7)), so the MFMA B-operand
+//    reads (lane: token t, 32 bytes) hit distinct banks.  The fp32 scales go
+//    to VGPRs (one token per lane) and reach the epilogue lanes by shuffle;
+//  * an instruction's 8 tokens always lie in one page (pages hold >= 8
+//    tokens), so its page base is wave-uniform: pages smaller than the 16-token
+//    matrix tile are assembled into one tile (aiter PR #6626 section 1 builds a
+//    tile from several 8-token pages).  Page ids are read one iteration ahead
+//    of the gather, itself 4 iterations ahead of the matrix work;
 //  * page byte offsets are int64 (id * page_size * 132) and the output row
 //    base is int64 (row * out_row_stride) with int32 columns, so pools and
 //    outputs beyond 2^31 bytes are addressed correctly (aiter PR #4244 "Fix";
 //    ATOM PR #2533 "Address Triton decode KV rows with int64 ids");
 //  * workgroups are dealt round-robin over the 8 XCDs, so the grid is
-//    re-indexed to give each XCD a contiguous run of units: a request's
-//    chunks share one L2, which keeps its q and table warm.
+//    re-indexed to give each XCD a contiguous run of waves: neighbouring runs
+//    of iterations (mostly the same requests) share one L2, which keeps their
+//    q and table rows warm.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "pmqa_internal.h"
 
@@ -44,27 +59,19 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// K records are 132 bytes, so a token's bytes are only 4-byte aligned.
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4))) __attribute__((aligned(4)));
 
 constexpr int kTile = 16;                 // tokens per MFMA tile (N)
 constexpr int kTilesPerIter = 4;          // 64 tokens: one per lane at store time
 constexpr int kIterTokens = kTile * kTilesPerIter;
-constexpr int kWaveTokens = 256;          // tokens per wave unit
-constexpr int kWavesPerGroup = 4;         // waves per workgroup
-constexpr int kThreads = 64 * kWavesPerGroup;
+constexpr int kSlotValueBytes = kIterTokens * 128;     // K values of one iteration
+constexpr int kSlotBytes = kSlotValueBytes + kIterTokens * 4;  // + its fp32 scales
+constexpr int kDmaPerIter = kIterTokens / 8;   // 8 tokens per 64-lane 16-byte load
+constexpr int kGatherLoads = kDmaPerIter + 1;  // vector memory instructions per gather
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 __device__ __forceinline__ v8i load_q32(const uint8_t* p) {
   const u32x4* v = reinterpret_cast<const u32x4*>(p);  // 32-byte aligned
-  u32x4 a = v[0], b = v[1];
-  v8i r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-  return r;
-}
-
-__device__ __forceinline__ v8i load_k32(const uint8_t* p) {
-  const u32x4_a4* v = reinterpret_cast<const u32x4_a4*>(p);  // 4-byte aligned
   u32x4 a = v[0], b = v[1];
   v8i r;
   r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
@@ -116,188 +123,528 @@ __device__ __forceinline__ v4f mfma_exact(v8i a, const v8h (&b)[4]) {
 // row's largest score, while rows of 32 tokens or more stay near 4e-5.
 constexpr int kExactRows = 128;
 
-struct UnitCtx {
-  const uint8_t* kv;
-  float* out;
-  int64_t out_stride;
-  int64_t page_base;  // lane i: byte offset of the unit's i-th page
-  int b, ctx, ctx_eff, t_begin, t_end, j0, next_n, p_first, lp, in_page_mask, lane, m, kq;
-};
-
-template <int H, int JW, bool EXACT>
-__device__ __forceinline__ void run_unit(const UnitCtx& u, const v8i (&qa)[JW][H / 16],
-                                         const v4f (&wv)[JW][H / 16]) {
-  constexpr int HT = H / 16;
-  const float neg_inf = -__builtin_inff();
-  for (int it0 = u.t_begin; it0 < u.t_end; it0 += kIterTokens) {
-    // addresses first (lanes past the unit's end read the pool's first record,
-    // and their results are never stored), then every load of the iteration
-    int64_t off[kTilesPerIter];
-#pragma unroll
-    for (int tile = 0; tile < kTilesPerIter; ++tile) {
-      const int t = it0 + tile * kTile + u.m;
-      const bool valid = t < u.t_end;
-      const int slot = valid ? (t >> u.lp) - u.p_first : 0;
-      const int64_t base = __shfl(u.page_base, slot);
-      const int64_t o = base + (int32_t)((t & u.in_page_mask) * kRecordBytes);
-      off[tile] = valid ? o : int64_t{0};
-    }
-    v8i kb[kTilesPerIter];
-    float ks[kTilesPerIter];
-#pragma unroll
-    for (int tile = 0; tile < kTilesPerIter; ++tile) {
-      const uint8_t* rec = u.kv + off[tile];
-      kb[tile] = load_k32(rec + u.kq * 32);
-      ks[tile] = *reinterpret_cast<const float*>(rec + kHeadDim);
-    }
-
-    float keep[JW];
-#pragma unroll
-    for (int jj = 0; jj < JW; ++jj) keep[jj] = 0.f;
-#pragma unroll
-    for (int tile = 0; tile < kTilesPerIter; ++tile) {
-      const float s = ks[tile];
-      v8h kh[4];
-      if constexpr (EXACT) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kh[c] = fp8x8_to_f16(kb[tile][2 * c], kb[tile][2 * c + 1]);
-      }
-#pragma unroll
-      for (int jj = 0; jj < JW; ++jj) {
-        float sum = 0.f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          v4f acc;
-          if constexpr (EXACT) acc = mfma_exact(qa[jj][ht], kh);
-          else acc = mfma_fp8(qa[jj][ht], kb[tile]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sum = __builtin_fmaf(wv[jj][ht][i], __builtin_fmaxf(acc[i] * s, 0.f), sum);
-        }
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        if (u.kq == tile) keep[jj] = sum;
-      }
-    }
-
-    const int t = it0 + u.lane;
-#pragma unroll
-    for (int jj = 0; jj < JW; ++jj) {
-      const int j = u.j0 + jj;
-      if (j >= u.next_n) break;
-      const int vis = min(max(u.ctx - u.next_n + j + 1, 0), u.ctx_eff);
-      float* orow = u.out + ((int64_t)u.b * u.next_n + j) * u.out_stride;
-      if (t < vis)
-        orow[t] = keep[jj];
-      else if (t < u.ctx_eff)
-        orow[t] = neg_inf;
-    }
-  }
+// Number of 64-token iterations of a context (clamped to the grid's bound).
+__device__ __forceinline__ int n_iters(int ctx, int max_tokens) {
+  const int c = min(max(ctx, 0), max_tokens);
+  return (c + kIterTokens - 1) / kIterTokens;
 }
 
-// H heads; JW next_n rows per wave.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The context lengths of 64 consecutive requests, one per lane, so that the
+// wave can step from request to request without a memory round trip inside
+// its pipeline (a load there would make the compiler drain every in-flight
+// gather).  Reloaded, with an explicit full wait, when a wave's run crosses
+// into the next 64 requests.
+struct CtxWindow {
+  int c0;   // first request held
+  int len;  // lane i: context length of request c0 + i (0 past the batch)
+};
+
+__device__ __forceinline__ void load_window(const LogitsParams& p, int c0, int lane, CtxWindow& w) {
+  w.c0 = c0;
+  w.len = c0 + lane < p.batch ? max(p.ctx[c0 + lane], 0) : 0;
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Position in the iteration list: request b, iteration it, and b's length
+// (all wave-uniform).
+struct Cursor {
+  int b, it, ctx, ctx_eff;
+};
+
+// Cursor at iteration it of request b.  Requests inside the window come from
+// its lanes; one outside it (the page-id walk runs ahead of the gather walk
+// and may already have moved the window on) is read from memory, with an
+// explicit full wait.
+__device__ __forceinline__ Cursor cursor_at(const LogitsParams& p, const CtxWindow& w, int b,
+                                            int it) {
+  Cursor c;
+  c.b = b;
+  c.it = it;
+  if ((unsigned)(b - w.c0) < 64u) {
+    c.ctx = __builtin_amdgcn_readlane(w.len, b - w.c0);
+  } else {
+    c.ctx = uniform(max(p.ctx[b], 0));
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  c.ctx_eff = min(c.ctx, p.max_tokens);
+  return c;
+}
+
+// Next iteration in the list (skips requests with nothing to score).  Only
+// called while iterations remain, so a non-empty request always follows.
+__device__ __forceinline__ Cursor advance(const LogitsParams& p, CtxWindow& w, int lane,
+                                          Cursor c) {
+  if ((c.it + 1) * kIterTokens < c.ctx_eff) {
+    ++c.it;
+    return c;
+  }
+  int b = c.b;
+  Cursor n;
+  do {
+    ++b;
+    if (b - w.c0 == 64) load_window(p, b, lane, w);  // first step past the window
+    n = cursor_at(p, w, b, 0);
+  } while (n.ctx_eff == 0 && b + 1 < p.batch);
+  return n;
+}
+
 template <int H, int JW>
-__global__ __launch_bounds__(kThreads) void logits_kernel(LogitsParams p) {
-  constexpr int HT = H / 16;  // 16-head A tiles per row
-  UnitCtx u;
-  u.lane = threadIdx.x & 63;
-  u.m = u.lane & 15;   // token within a tile (B column / A row)
-  u.kq = u.lane >> 4;  // 32-byte quarter of the head dimension
-  const uint32_t nwg = gridDim.x;  // a multiple of 8
-  const uint32_t wg = (blockIdx.x & 7u) * (nwg >> 3) + (blockIdx.x >> 3);
-  const uint32_t unit = wg * kWavesPerGroup + (threadIdx.x >> 6);
-  if (unit >= p.n_units) return;
+struct QRegs {
+  v8i qa[JW][H / 16];
+  v4f wv[JW][H / 16];
+  int b;  // request whose q rows are loaded
+};
 
-  const int g = (int)(unit % (uint32_t)p.n_rgroups);
-  const uint32_t bc = unit / (uint32_t)p.n_rgroups;
-  const int c = (int)(bc % (uint32_t)p.n_chunks);
-  u.b = (int)(bc / (uint32_t)p.n_chunks);
-  u.ctx = max(p.ctx[u.b], 0);
-  u.ctx_eff = min(u.ctx, p.max_tokens);
-  u.t_begin = c * kWaveTokens;
-  if (u.t_begin >= u.ctx_eff) return;
-  u.t_end = min(u.t_begin + kWaveTokens, u.ctx_eff);
-  u.j0 = g * JW;
-  u.next_n = p.next_n;
-  u.kv = p.kv;
-  u.out = p.out;
-  u.out_stride = p.out_stride;
-
-  // q rows and weights of this unit, in MFMA A-operand order
-  v8i qa[JW][HT];
-  v4f wv[JW][HT];
+// Load q rows and weights of request b and wait for them (an explicit full
+// wait, so no later code needs a compiler-inserted one).
+template <int H, int JW>
+__device__ __forceinline__ void load_q(const LogitsParams& p, int b, int j0, int m, int kq,
+                                       QRegs<H, JW>& qr) {
+  constexpr int HT = H / 16;
 #pragma unroll
   for (int jj = 0; jj < JW; ++jj) {
-    const int j = min(u.j0 + jj, u.next_n - 1);  // rows past next_n are never stored
-    const int64_t row = (int64_t)u.b * u.next_n + j;
+    const int j = min(j0 + jj, p.next_n - 1);  // rows past next_n are never stored
+    const int64_t row = (int64_t)b * p.next_n + j;
     const uint8_t* qrow = p.q + row * (int64_t)(H * kHeadDim);
     const float* wrow = p.w + row * H;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      qa[jj][ht] = load_q32(qrow + (ht * 16 + u.m) * kHeadDim + u.kq * 32);
-      wv[jj][ht] = *reinterpret_cast<const v4f*>(wrow + ht * 16 + u.kq * 4);
+      qr.qa[jj][ht] = load_q32(qrow + (ht * 16 + m) * kHeadDim + kq * 32);
+      qr.wv[jj][ht] = *reinterpret_cast<const v4f*>(wrow + ht * 16 + kq * 4);
     }
   }
+  qr.b = b;
+  __builtin_amdgcn_s_waitcnt(0);
+}
 
-  // page ids of the unit, one per lane (at most 32 for 8-token pages)
-  u.lp = p.log2_page;
-  u.p_first = u.t_begin >> u.lp;
-  const int n_pg = ((u.t_end - 1) >> u.lp) - u.p_first + 1;
-  u.page_base = 0;
-  if (u.lane < n_pg)
-    u.page_base = p.tables[(int64_t)u.b * p.table_stride + u.p_first + u.lane] * p.page_bytes;
-  u.in_page_mask = p.page_size - 1;
+// Page ids of an iteration, gathered into LDS by one 4-byte-per-lane load:
+// lanes 2i and 2i+1 move the two halves of the iteration's i-th page id.
+// Only ids inside the context are read (at most 8 pages per iteration).
+__device__ __forceinline__ void issue_ids(const LogitsParams& p, const Cursor& c, int lane,
+                                          int64_t* ids_slot) {
+  const int t0 = c.it * kIterTokens;
+  const int lp = p.log2_page;
+  const int p_first = t0 >> lp;
+  const int n_pg = ((min(t0 + kIterTokens, c.ctx_eff) - 1) >> lp) - p_first + 1;
+  const uint32_t* row =
+      reinterpret_cast<const uint32_t*>(p.tables + (int64_t)c.b * p.table_stride + p_first);
+  if (lane < 2 * n_pg) __builtin_amdgcn_global_load_lds(row + lane, LDS_PTR(ids_slot), 4, 0, 0);
+}
 
-  // the unit's first row sees the fewest tokens
-  const int min_vis = min(max(u.ctx - u.next_n + u.j0 + 1, 0), u.ctx);
-  if (min_vis < kExactRows)
-    run_unit<H, JW, true>(u, qa, wv);
-  else
-    run_unit<H, JW, false>(u, qa, wv);
+// Pages of an iteration's gather, read from its LDS id slot: the page under
+// each 8-token group (wave-uniform) and the page under this lane's token.  An
+// iteration starts at a multiple of 64 tokens and pages hold 8..256 tokens,
+// so token t0 + x lies in page (x >> log2_page) of the iteration.
+struct GatherPages {
+  int64_t group[kDmaPerIter];
+  int64_t lane;
+};
+
+// Inline assembly with its own LDS wait on purpose: the compiler cannot tell
+// which in-flight LDS-bound loads a plain LDS read could alias and would drain
+// every one of them first, while the ring's ordering already proves these ids
+// have landed.
+__device__ __forceinline__ GatherPages read_pages(const int64_t* ids_slot, int lp, int lane) {
+  const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const int64_t*)ids_slot);
+  uint32_t g[kDmaPerIter];
+#pragma unroll
+  for (int i = 0; i < kDmaPerIter; ++i) g[i] = a + 8u * (uint32_t)((8 * i) >> lp);
+  const uint32_t al = a + 8u * (uint32_t)(lane >> lp);
+  GatherPages r;
+  asm volatile(
+      "ds_read_b64 %0, %9\n\t"
+      "ds_read_b64 %1, %10\n\t"
+      "ds_read_b64 %2, %11\n\t"
+      "ds_read_b64 %3, %12\n\t"
+      "ds_read_b64 %4, %13\n\t"
+      "ds_read_b64 %5, %14\n\t"
+      "ds_read_b64 %6, %15\n\t"
+      "ds_read_b64 %7, %16\n\t"
+      "ds_read_b64 %8, %17\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.group[0]), "=&v"(r.group[1]), "=&v"(r.group[2]), "=&v"(r.group[3]),
+        "=&v"(r.group[4]), "=&v"(r.group[5]), "=&v"(r.group[6]), "=&v"(r.group[7]),
+        "=&v"(r.lane)
+      : "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]), "v"(g[4]), "v"(g[5]), "v"(g[6]), "v"(g[7]),
+        "v"(al)
+      : "memory");
+  return r;
+}
+
+// Issue the gather of one iteration into an LDS slot: 8 loads of 16 bytes per
+// lane for the values (8 tokens per instruction; a page holds at least 8
+// tokens, so an instruction's tokens share one page) and one of 4 bytes per
+// lane for the scales (token = lane).  Exactly kGatherLoads vector memory
+// instructions are issued on every call: lanes past the context fetch the
+// pool's first record instead, and their results are never stored.
+__device__ __forceinline__ void issue_gather(const LogitsParams& p, const Cursor& c,
+                                             const int64_t* ids_slot, int lane, uint8_t* slot) {
+  const int t0 = c.it * kIterTokens;
+  const int in_page_mask = p.page_size - 1;
+  const int sub = lane >> 3;                 // token within the instruction's 8
+  const int chunk = (lane & 7) ^ sub;        // swizzled 16-byte chunk this lane moves
+  const GatherPages pg = read_pages(ids_slot, p.log2_page, lane);
+#pragma unroll
+  for (int i = 0; i < kDmaPerIter; ++i) {
+    const int t = t0 + 8 * i + sub;
+    const int64_t off = t < c.ctx_eff ? pg.group[i] * p.page_bytes +
+                                            (int32_t)((t & in_page_mask) * kRecordBytes) + 16 * chunk
+                                      : (int64_t)(16 * chunk);
+    __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * 1024), 16, 0, 0);
+  }
+  const int t = t0 + lane;
+  const int64_t soff =
+      t < c.ctx_eff ? pg.lane * p.page_bytes + (int32_t)((t & in_page_mask) * kRecordBytes) : 0;
+  __builtin_amdgcn_global_load_lds(p.kv + soff + kHeadDim, LDS_PTR(slot + kSlotValueBytes), 4,
+                                   0, 0);
+}
+
+// Wait until at most n vector memory instructions are outstanding (n one of
+// the values the ring produces, a multiple of kGatherLoads below 4 of them;
+// anything smaller waits for all).
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 3 * kGatherLoads) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+  else if (n >= 2 * kGatherLoads) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if (n >= kGatherLoads) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Sum of the value held by lanes l, l^16, l^32 and l^48 (the four 16-lane rows
+// of the wave), on every lane: two row swaps, no LDS traffic.
+__device__ __forceinline__ float sum_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Score one iteration (64 tokens x the wave's rows) from its LDS slot and
+// store it.  FACTORED: every scale of the iteration is >= 0, so
+// relu(s * x) = s * relu(x) and the scale multiplies the head-weighted sum once
+// per token instead of once per head (2 VALU operations per MFMA output
+// instead of 3); otherwise the literal form runs.
+template <int H, int JW, bool EXACT, bool FACTORED>
+__device__ __forceinline__ void score_iteration(const LogitsParams& p, const Cursor& c, int j0,
+                                                int lane, const QRegs<H, JW>& qr,
+                                                const uint8_t* slot) {
+  constexpr int HT = H / 16;
+  const int m = lane & 15, kq = lane >> 4;
+  const float* scales = reinterpret_cast<const float*>(slot + kSlotValueBytes);
+  const int t0 = c.it * kIterTokens;
+  // B operands and scales of the 4 tiles
+  v8i kb[kTilesPerIter];
+  float sc[kTilesPerIter];
+#pragma unroll
+  for (int tile = 0; tile < kTilesPerIter; ++tile) {
+    const int tl = tile * kTile + m;
+    const uint8_t* row = slot + tl * 128;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(row + 16 * ((2 * kq) ^ (m & 7)));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 16 * ((2 * kq + 1) ^ (m & 7)));
+    kb[tile][0] = lo[0]; kb[tile][1] = lo[1]; kb[tile][2] = lo[2]; kb[tile][3] = lo[3];
+    kb[tile][4] = hi[0]; kb[tile][5] = hi[1]; kb[tile][6] = hi[2]; kb[tile][7] = hi[3];
+    sc[tile] = t0 + tl < c.ctx_eff ? scales[tl] : 0.f;  // tokens past the context: 0
+  }
+  float keep[JW];
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) keep[jj] = 0.f;
+#pragma unroll
+  for (int tile = 0; tile < kTilesPerIter; ++tile) {
+    const float s = sc[tile];
+    v8h kh[4];
+    if constexpr (EXACT) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kh[q] = fp8x8_to_f16(kb[tile][2 * q], kb[tile][2 * q + 1]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+      v4f acc[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        if constexpr (EXACT) acc[ht] = mfma_exact(qr.qa[jj][ht], kh);
+        else acc[ht] = mfma_fp8(qr.qa[jj][ht], kb[tile]);
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (FACTORED)
+            sum = __builtin_fmaf(qr.wv[jj][ht][i], __builtin_fmaxf(acc[ht][i], 0.f), sum);
+          else
+            sum = __builtin_fmaf(qr.wv[jj][ht][i], __builtin_fmaxf(acc[ht][i] * s, 0.f), sum);
+        }
+      }
+      sum = sum_rows(sum);
+      if constexpr (FACTORED) sum *= s;
+      if (kq == tile) keep[jj] = sum;
+    }
+  }
+  const float neg_inf = -__builtin_inff();
+  const int t = t0 + lane;
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) {
+    const int j = j0 + jj;
+    if (j >= p.next_n) break;
+    const int vis = min(max(c.ctx - p.next_n + j + 1, 0), c.ctx_eff);
+    float* orow = p.out + ((int64_t)c.b * p.next_n + j) * p.out_stride;
+    if (t < vis)
+      orow[t] = keep[jj];
+    else if (t < c.ctx_eff)
+      orow[t] = neg_inf;
+  }
 }
 
 template <int H, int JW>
-hipError_t launch_one(const LogitsParams& p, hipStream_t stream) {
-  uint32_t n_wg = (p.n_units + kWavesPerGroup - 1) / kWavesPerGroup;
+__device__ __forceinline__ void score(const LogitsParams& p, const Cursor& c, int j0, int lane,
+                                      const QRegs<H, JW>& qr, const uint8_t* slot) {
+  // the wave's first row sees the fewest tokens
+  const int min_vis = min(max(c.ctx - p.next_n + j0 + 1, 0), c.ctx);
+  // scales of the iteration's tokens (one per lane), past the context: 0
+  const float* scales = reinterpret_cast<const float*>(slot + kSlotValueBytes);
+  const float s = c.it * kIterTokens + lane < c.ctx_eff ? scales[lane] : 0.f;
+  const bool factored = __ballot(!(s >= 0.f)) == 0;  // NaN also takes the literal form
+  if (min_vis < kExactRows) {
+    if (factored) score_iteration<H, JW, true, true>(p, c, j0, lane, qr, slot);
+    else score_iteration<H, JW, true, false>(p, c, j0, lane, qr, slot);
+  } else {
+    if (factored) score_iteration<H, JW, false, true>(p, c, j0, lane, qr, slot);
+    else score_iteration<H, JW, false, false>(p, c, j0, lane, qr, slot);
+  }
+}
+
+// H heads; JW next_n rows per wave; WAVES waves per workgroup (one workgroup
+// per CU); RING iterations in flight per wave.
+//
+// Pipeline of one wave (refill(j) = page ids of iteration j+2R, then the gather
+// of iteration j+R; R = RING):
+//   prologue: ids of iterations 0..R-1 and the q rows (waited for),
+//             refill(-R) .. refill(-1)
+//   loop k:   wait for gather k; score k from its slot; refill(k)
+// The ids refill(k) uses (those of iteration k+R) were issued by refill(k-R)
+// before the gather of k, so "gather k has landed" (the vector memory counter
+// drains in order) also proves they have landed.  Ids of iteration j live in
+// id slot j % 2R, values in ring slot j % R.
+template <int H, int JW, int WAVES, int RING>
+__global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][RING][kSlotBytes];
+  __shared__ __attribute__((aligned(16))) int64_t ids[WAVES][2 * RING][kDmaPerIter];
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15;   // token within a tile (B column / A row)
+  const int kq = lane >> 4;  // 32-byte quarter of the head dimension
+  const int wl = threadIdx.x >> 6;
+  const uint32_t nwg = gridDim.x;  // a multiple of 8
+  const uint32_t wg = (blockIdx.x & 7u) * (nwg >> 3) + (blockIdx.x >> 3);
+  const uint32_t wave = wg * WAVES + wl;
+  if (wave >= (uint32_t)p.n_slices * (uint32_t)p.n_rgroups) return;
+  const int slice = (int)(wave / (uint32_t)p.n_rgroups);
+  const int j0 = (int)(wave % (uint32_t)p.n_rgroups) * JW;
+
+  // this slice's share [lo, hi) of the iteration list, and the 64 context
+  // lengths around its start
+  CtxWindow win;
+  Cursor first;
+  int64_t lo, hi;
+  if (p.batch <= 64) {
+    // one load: the whole batch is the window
+    win.c0 = 0;
+    win.len = lane < p.batch ? max(p.ctx[lane], 0) : 0;
+    const int n = n_iters(win.len, p.max_tokens);
+    const int incl = wave_incl_scan(n, lane);
+    const int64_t total = uniform(__shfl(incl, 63));
+    lo = total * slice / p.n_slices;
+    hi = total * (slice + 1) / p.n_slices;
+    if (lo >= hi) return;
+    const uint64_t past = __ballot(incl > lo);
+    const int f = uniform(__builtin_ctzll(past));
+    const int incl_f = uniform(__shfl(incl, f));
+    const int n_f = uniform(__shfl(n, f));
+    first = cursor_at(p, win, f, (int)(lo - (incl_f - n_f)));
+  } else {
+    int64_t total = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += 64) {
+      const int b = c0 + lane;
+      total += uniform(wave_sum(b < p.batch ? n_iters(p.ctx[b], p.max_tokens) : 0));
+    }
+    lo = total * slice / p.n_slices;
+    hi = total * (slice + 1) / p.n_slices;
+    if (lo >= hi) return;
+    int64_t before = 0;
+    for (int c0 = 0;; c0 += 64) {
+      const int b = c0 + lane;
+      const int n = b < p.batch ? n_iters(p.ctx[b], p.max_tokens) : 0;
+      const int incl = wave_incl_scan(n, lane);
+      const int chunk = uniform(__shfl(incl, 63));
+      if (before + chunk > lo) {
+        const uint64_t past = __ballot(before + incl > lo);
+        const int f = uniform(__builtin_ctzll(past));
+        const int incl_f = uniform(__shfl(incl, f));
+        const int n_f = uniform(__shfl(n, f));
+        load_window(p, c0 + f, lane, win);
+        first = cursor_at(p, win, c0 + f, (int)(lo - (before + incl_f - n_f)));
+        break;
+      }
+      before += chunk;
+    }
+  }
+  const int n_it = (int)(hi - lo);
+  uint8_t* my_ring = &ring[wl][0][0];
+  int64_t* my_ids = &ids[wl][0][0];
+
+  // prologue: ids of the first RING iterations and the q rows, waited for together
+  Cursor cs[RING];  // iteration scored from ring slot s: k with k % RING == s
+  cs[0] = first;
+#pragma unroll
+  for (int s = 1; s < RING; ++s) cs[s] = s < n_it ? advance(p, win, lane, cs[s - 1]) : cs[s - 1];
+#pragma unroll
+  for (int s = 0; s < RING; ++s)
+    if (s < n_it) issue_ids(p, cs[s], lane, my_ids + s * kDmaPerIter);
+  QRegs<H, JW> qr;
+  load_q<H, JW>(p, first.b, j0, m, kq, qr);  // ends with a full wait
+  Cursor ahead = cs[RING - 1];  // last iteration whose ids were issued
+  int n_ids = min(n_it, RING);  // iterations whose ids were issued
+#pragma unroll
+  for (int s = 0; s < RING; ++s) {
+    if (s < n_it) {
+      // refill(s - R): ids of iteration s + R, then the gather of s
+      if (n_ids < n_it) {
+        ahead = advance(p, win, lane, ahead);
+        issue_ids(p, ahead, lane, my_ids + (n_ids % (2 * RING)) * kDmaPerIter);
+        ++n_ids;
+      }
+      issue_gather(p, cs[s], my_ids + s * kDmaPerIter, lane, my_ring + s * kSlotBytes);
+    }
+  }
+
+  for (int k0 = 0; k0 < n_it; k0 += RING) {
+#pragma unroll
+    for (int s = 0; s < RING; ++s) {
+      const int k = k0 + s;
+      if (k >= n_it) break;
+      // the gathers of iterations k+1 .. min(k+R-1, n_it-1) were issued after
+      // this one's, kGatherLoads instructions each (page-id loads and stores
+      // issued in between only add to the count): once at most that many are
+      // outstanding, iteration k's data has landed in its slot
+      wait_vm(kGatherLoads * min(RING - 1, n_it - 1 - k));
+      if (cs[s].b != qr.b) load_q<H, JW>(p, cs[s].b, j0, m, kq, qr);
+      score<H, JW>(p, cs[s], j0, lane, qr, my_ring + s * kSlotBytes);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot reads done before refill
+      if (k + RING < n_it) {
+        // refill(k): ids of iteration k + 2R, then the gather of k + R
+        const Cursor g = advance(p, win, lane, cs[(s + RING - 1) % RING]);
+        if (n_ids < n_it) {
+          ahead = advance(p, win, lane, ahead);
+          issue_ids(p, ahead, lane, my_ids + (n_ids % (2 * RING)) * kDmaPerIter);
+          ++n_ids;
+        }
+        cs[s] = g;
+        issue_gather(p, g, my_ids + ((k + RING) % (2 * RING)) * kDmaPerIter, lane,
+                     my_ring + s * kSlotBytes);
+      }
+    }
+  }
+}
+
+// Launch geometry per instantiation: wave units of at most 64 q rows run two
+// waves per SIMD (8 per workgroup, 2 iterations in flight each) so that one
+// wave's matrix work overlaps the other's memory stalls; larger ones need the
+// registers of a whole SIMD and run 4 waves per workgroup with 4 in flight.
+template <int H, int JW>
+struct Geometry {
+  static constexpr bool kSmall = H * JW <= 64;
+  static constexpr int kWaves = kSmall ? 8 : 4;
+  static constexpr int kRingDepth = kSmall ? 2 : 4;
+};
+
+template <int H, int JW>
+hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t stream) {
+  using G = Geometry<H, JW>;
+  uint32_t n_wg = ((uint32_t)p.n_slices * (uint32_t)p.n_rgroups + G::kWaves - 1) / G::kWaves;
   n_wg = (n_wg + 7u) & ~7u;
-  hipLaunchKernelGGL((logits_kernel<H, JW>), dim3(n_wg), dim3(kThreads), 0, stream, p);
+  auto kern = logits_kernel<H, JW, G::kWaves, G::kRingDepth>;
+  if (tm.start || tm.stop)
+    hipExtLaunchKernelGGL(kern, dim3(n_wg), dim3(64 * G::kWaves), 0, stream, tm.start, tm.stop, 0,
+                          p);
+  else
+    hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64 * G::kWaves), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int H>
-hipError_t launch_heads(const LogitsParams& p, int jw, hipStream_t stream) {
+hipError_t launch_heads(const LogitsParams& p, int jw, const LaunchTiming& tm,
+                        hipStream_t stream) {
   if constexpr (H <= 64) {
     switch (jw) {
-      case 1: return launch_one<H, 1>(p, stream);
-      case 2: return launch_one<H, 2>(p, stream);
-      case 3: return launch_one<H, 3>(p, stream);
-      case 4: return launch_one<H, 4>(p, stream);
+      case 1: return launch_one<H, 1>(p, tm, stream);
+      case 2: return launch_one<H, 2>(p, tm, stream);
+      case 3: return launch_one<H, 3>(p, tm, stream);
+      case 4: return launch_one<H, 4>(p, tm, stream);
     }
   } else {
     switch (jw) {
-      case 1: return launch_one<H, 1>(p, stream);
-      case 2: return launch_one<H, 2>(p, stream);
+      case 1: return launch_one<H, 1>(p, tm, stream);
+      case 2: return launch_one<H, 2>(p, tm, stream);
     }
   }
   return hipErrorInvalidValue;
 }
 
-}  // namespace
-
-int logits_wave_tokens() { return kWaveTokens; }
-
-int logits_rows_per_wave(int heads, int next_n) {
-  // at most 256 q rows (128 VGPRs of A operands) per wave
-  const int cap = heads >= 128 ? 1 : (heads >= 64 ? 3 : 4);
-  return next_n < cap ? next_n : cap;
+template <int H>
+int waves_per_cu(int jw) {
+  switch (jw) {
+    case 1: return Geometry<H, 1>::kWaves;
+    case 2: return Geometry<H, 2>::kWaves;
+    case 3: return Geometry<H, 3>::kWaves;
+    default: return Geometry<H, 4>::kWaves;
+  }
 }
 
-hipError_t launch_logits(const LogitsParams& p, int heads, int jw, hipStream_t stream) {
+}  // namespace
+
+LogitsShape logits_shape(int heads, int next_n) {
+  LogitsShape sh;
+  // at most 256 q rows (128 VGPRs of A operands) per wave
+  const int cap = heads >= 128 ? 1 : (heads >= 64 ? 3 : 4);
+  sh.rows_per_wave = next_n < cap ? next_n : cap;
+  sh.iter_tokens = kIterTokens;
+  // one workgroup per CU (its K ring fills most of the CU's LDS)
+  int per_cu = 4;
   switch (heads) {
-    case 16: return launch_heads<16>(p, jw, stream);
-    case 32: return launch_heads<32>(p, jw, stream);
-    case 64: return launch_heads<64>(p, jw, stream);
-    case 128: return launch_heads<128>(p, jw, stream);
+    case 16: per_cu = waves_per_cu<16>(sh.rows_per_wave); break;
+    case 32: per_cu = waves_per_cu<32>(sh.rows_per_wave); break;
+    case 64: per_cu = waves_per_cu<64>(sh.rows_per_wave); break;
+    case 128: per_cu = waves_per_cu<128>(sh.rows_per_wave); break;
+  }
+  sh.target_waves = 256 * per_cu;
+  if (const char* e = getenv("PMQA_LOGITS_WAVES")) sh.target_waves = atoi(e);
+  return sh;
+}
+
+hipError_t launch_logits(const LogitsParams& p, const LogitsShape& sh, int heads,
+                         const LaunchTiming& tm, hipStream_t stream) {
+  switch (heads) {
+    case 16: return launch_heads<16>(p, sh.rows_per_wave, tm, stream);
+    case 32: return launch_heads<32>(p, sh.rows_per_wave, tm, stream);
+    case 64: return launch_heads<64>(p, sh.rows_per_wave, tm, stream);
+    case 128: return launch_heads<128>(p, sh.rows_per_wave, tm, stream);
   }
   return hipErrorInvalidValue;
 }

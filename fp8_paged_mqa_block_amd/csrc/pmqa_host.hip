@@ -37,11 +37,15 @@ const char* pmqa_status_string(pmqa_status status) {
 
 int32_t pmqa_version(void) { return 100; }
 
-pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const float* weights,
-                             const int32_t* context_lens, const int64_t* block_tables,
-                             int32_t page_size, int32_t next_n, float* out,
-                             int64_t out_row_stride, int32_t batch, int32_t num_heads,
-                             int32_t head_dim, int64_t block_table_stride, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weights,
+                        const int32_t* context_lens, const int64_t* block_tables,
+                        int32_t page_size, int32_t next_n, float* out, int64_t out_row_stride,
+                        int32_t batch, int32_t num_heads, int32_t head_dim,
+                        int64_t block_table_stride, void* stream, const pmqa::LaunchTiming& tm) {
   if (batch < 0 || next_n < 1 || out_row_stride < 1 || block_table_stride < 1)
     return PMQA_ERR_SHAPE;
   if (!(page_size == 8 || page_size == 16 || page_size == 32 || page_size == 64 ||
@@ -78,24 +82,25 @@ pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const float* w
   if (out_row_stride < max_tokens) max_tokens = out_row_stride;
   if (max_tokens > INT32_MAX) max_tokens = INT32_MAX;
   p.max_tokens = (int32_t)max_tokens;
-  const int wave_tokens = pmqa::logits_wave_tokens();
-  const int64_t n_chunks = (max_tokens + wave_tokens - 1) / wave_tokens;
-  const int jw = pmqa::logits_rows_per_wave(num_heads, next_n);
-  const int64_t n_rgroups = (next_n + jw - 1) / jw;
-  const int64_t n_units = (int64_t)batch * n_chunks * n_rgroups;
-  if (n_units > (int64_t)UINT32_MAX / 2) return PMQA_ERR_SHAPE;
-  p.n_chunks = (int32_t)n_chunks;
+  const pmqa::LogitsShape sh = pmqa::logits_shape(num_heads, next_n);
+  const int64_t n_rgroups = (next_n + sh.rows_per_wave - 1) / sh.rows_per_wave;
+  // the persistent grid: enough runs to fill the chip, never more than the
+  // iterations the contexts could hold
+  const int64_t max_iters = (int64_t)batch * ((max_tokens + sh.iter_tokens - 1) / sh.iter_tokens);
+  int64_t n_slices = sh.target_waves / n_rgroups;
+  if (n_slices < 1) n_slices = 1;
+  if (n_slices > max_iters) n_slices = max_iters;
+  p.n_slices = (int32_t)n_slices;
   p.n_rgroups = (int32_t)n_rgroups;
-  p.n_units = (uint32_t)n_units;
   if (!is_pow2(page_size)) return PMQA_ERR_SHAPE;
 
-  hipError_t e = pmqa::launch_logits(p, num_heads, jw, static_cast<hipStream_t>(stream));
+  hipError_t e = pmqa::launch_logits(p, sh, num_heads, tm, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
 }
 
-pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,
-                         int32_t* out_idx, int32_t batch, int32_t next_n,
-                         int64_t logits_row_stride, void* stream) {
+pmqa_status topk_impl(const float* logits, const int32_t* context_lens, int32_t k,
+                      int32_t* out_idx, int32_t batch, int32_t next_n, int64_t logits_row_stride,
+                      void* stream, const pmqa::LaunchTiming& tm) {
   if (batch < 0 || next_n < 1 || logits_row_stride < 1) return PMQA_ERR_SHAPE;
   if (k < 1 || k > 2048) return PMQA_ERR_SHAPE;
   if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
@@ -111,8 +116,55 @@ pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32
   p.batch = batch;
   p.next_n = next_n;
   p.k = k;
-  hipError_t e = pmqa::launch_topk(p, static_cast<hipStream_t>(stream));
+  hipError_t e = pmqa::launch_topk(p, tm, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
+}
+
+pmqa::LaunchTiming timing(void* start_event, void* stop_event) {
+  pmqa::LaunchTiming tm;
+  tm.start = static_cast<hipEvent_t>(start_event);
+  tm.stop = static_cast<hipEvent_t>(stop_event);
+  return tm;
+}
+
+}  // namespace
+
+extern "C" {
+
+pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const float* weights,
+                             const int32_t* context_lens, const int64_t* block_tables,
+                             int32_t page_size, int32_t next_n, float* out,
+                             int64_t out_row_stride, int32_t batch, int32_t num_heads,
+                             int32_t head_dim, int64_t block_table_stride, void* stream) {
+  return logits_impl(q, kv_cache, weights, context_lens, block_tables, page_size, next_n, out,
+                     out_row_stride, batch, num_heads, head_dim, block_table_stride, stream,
+                     pmqa::LaunchTiming{});
+}
+
+pmqa_status paged_mqa_logits_timed(const void* q, const void* kv_cache, const float* weights,
+                                   const int32_t* context_lens, const int64_t* block_tables,
+                                   int32_t page_size, int32_t next_n, float* out,
+                                   int64_t out_row_stride, int32_t batch, int32_t num_heads,
+                                   int32_t head_dim, int64_t block_table_stride, void* stream,
+                                   void* start_event, void* stop_event) {
+  return logits_impl(q, kv_cache, weights, context_lens, block_tables, page_size, next_n, out,
+                     out_row_stride, batch, num_heads, head_dim, block_table_stride, stream,
+                     timing(start_event, stop_event));
+}
+
+pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,
+                         int32_t* out_idx, int32_t batch, int32_t next_n,
+                         int64_t logits_row_stride, void* stream) {
+  return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, stream,
+                   pmqa::LaunchTiming{});
+}
+
+pmqa_status topk_per_row_timed(const float* logits, const int32_t* context_lens, int32_t k,
+                               int32_t* out_idx, int32_t batch, int32_t next_n,
+                               int64_t logits_row_stride, void* stream, void* start_event,
+                               void* stop_event) {
+  return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, stream,
+                   timing(start_event, stop_event));
 }
 
 }  // extern "C"

@@ -26,18 +26,25 @@ struct LogitsParams {
   int32_t page_size;
   int32_t log2_page;
   int32_t max_tokens;      // min(table_stride*page_size, out_stride), clamped to int32
-  int32_t n_chunks;        // token chunks per request covered by the grid
-  int32_t n_rgroups;       // waves per chunk splitting the next_n rows
-  uint32_t n_units;        // batch * n_chunks * n_rgroups wave units
+  int32_t n_slices;        // runs of iterations the persistent grid splits the work into
+  int32_t n_rgroups;       // waves per run splitting the next_n rows
 };
 
-hipError_t launch_logits(const LogitsParams& p, int heads, int rows_per_wave_j,
-                         hipStream_t stream);
-// Number of MTP rows one wave holds for a given head count (the host uses it
-// to size the grid; the kernel is instantiated for exactly these).
-int logits_rows_per_wave(int heads, int next_n);
-// Tokens one wave unit covers.
-int logits_wave_tokens();
+// Optional events recorded by the kernel dispatch itself at its start and end.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Launch geometry chosen on the host for a head count and next_n.
+struct LogitsShape {
+  int rows_per_wave;  // next_n rows one wave holds (JW)
+  int iter_tokens;    // tokens per iteration of a wave
+  int target_waves;   // waves of the persistent grid when there is enough work
+};
+LogitsShape logits_shape(int heads, int next_n);
+hipError_t launch_logits(const LogitsParams& p, const LogitsShape& sh, int heads,
+                         const LaunchTiming& tm, hipStream_t stream);
 
 struct TopkParams {
   const float* logits;
@@ -49,6 +56,6 @@ struct TopkParams {
   int32_t k;
 };
 
-hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t stream);
 
 }  // namespace pmqa

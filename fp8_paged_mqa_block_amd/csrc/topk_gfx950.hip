@@ -13,6 +13,7 @@
 // runs only when equal keys outnumber the free slots).  Rows short enough to
 // fit are staged once into LDS so the passes do not re-read global memory.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -190,9 +191,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
+hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t stream) {
   const uint32_t rows = (uint32_t)p.batch * (uint32_t)p.next_n;
-  hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, p);
+  if (tm.start || tm.stop)
+    hipExtLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, tm.start, tm.stop,
+                          0, p);
+  else
+    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -26,8 +26,7 @@
  *
  * Conventions shared by every entry point:
  *   - every pointer argument is DEVICE memory owned by the caller; the library
- *     allocates nothing and keeps no state besides a per-device cache of the
- *     compute-unit count;
+ *     allocates nothing and keeps no state between calls;
  *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without synchronising; results are ordered only with
  *     later work on the same stream;
@@ -41,6 +40,12 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+#if defined(__GNUC__)
+#define PMQA_API __attribute__((visibility("default")))
+#else
+#define PMQA_API
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -73,9 +78,11 @@ typedef enum {
  * weights       [batch*next_n, num_heads] fp32, 16-byte aligned.
  * context_lens  [batch] int32, ctx_b >= 0 (negative values count as 0).
  * block_tables  [batch, block_table_stride] int64 page ids.  Only the first
- *               ceil(ctx_b/page_size) entries of row b are read; the rest may
- *               hold anything.  Preconditions not checked on the host (they
- *               live in device memory): read ids lie in [0, num_pages).
+ *               ceil(ctx_b/page_size) ids of row b are used; entries past them
+ *               may hold anything (the kernel may load them alongside the used
+ *               ones, never past the row's block_table_stride entries, and never
+ *               dereferences them).  Precondition not checked on the host (it
+ *               lives in device memory): used ids lie in [0, num_pages).
  * page_size     tokens per page: 8, 16, 32, 64, 128 or 256.  Pages smaller than
  *               the 16-token matrix tile are assembled into one tile (aiter
  *               PR #6626 section 1: a tile is built from several 8-token pages).
@@ -96,7 +103,7 @@ typedef enum {
  * kernel never reads past a table row nor writes past an output row, even
  * when the caller's context length exceeds them (a precondition violation).
  */
-pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const float* weights,
+PMQA_API pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const float* weights,
                              const int32_t* context_lens, const int64_t* block_tables,
                              int32_t page_size, int32_t next_n, float* out,
                              int64_t out_row_stride, int32_t batch, int32_t num_heads,
@@ -120,15 +127,38 @@ pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const float* w
  * logits_row_stride  elements between logits rows, >= 1.
  * stream        hipStream_t to enqueue on.
  */
-pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,
+PMQA_API pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,
                          int32_t* out_idx, int32_t batch, int32_t next_n,
                          int64_t logits_row_stride, void* stream);
 
+/*
+ * paged_mqa_logits_timed, topk_per_row_timed - the same operations, for callers
+ * that time each launch (benchmarks, serving telemetry).  start_event and
+ * stop_event are caller-created hipEvent_t handles (either may be NULL); they
+ * are recorded by the kernel dispatch itself when the kernel starts and when it
+ * ends (AMD's extended launch), so hipEventElapsedTime between them is the
+ * kernel's own duration, without the queue gaps that separate event records
+ * around a launch would add.  Arguments, checks and results are otherwise
+ * exactly those of the untimed calls.
+ */
+PMQA_API pmqa_status paged_mqa_logits_timed(const void* q, const void* kv_cache,
+                                            const float* weights, const int32_t* context_lens,
+                                            const int64_t* block_tables, int32_t page_size,
+                                            int32_t next_n, float* out, int64_t out_row_stride,
+                                            int32_t batch, int32_t num_heads, int32_t head_dim,
+                                            int64_t block_table_stride, void* stream,
+                                            void* start_event, void* stop_event);
+
+PMQA_API pmqa_status topk_per_row_timed(const float* logits, const int32_t* context_lens,
+                                        int32_t k, int32_t* out_idx, int32_t batch,
+                                        int32_t next_n, int64_t logits_row_stride, void* stream,
+                                        void* start_event, void* stop_event);
+
 /* Human-readable name of a status code (static storage; never NULL). */
-const char* pmqa_status_string(pmqa_status status);
+PMQA_API const char* pmqa_status_string(pmqa_status status);
 
 /* Library version, as major*10000 + minor*100 + patch. */
-int32_t pmqa_version(void);
+PMQA_API int32_t pmqa_version(void);
 
 #ifdef __cplusplus
 }
