@@ -5,13 +5,23 @@
 // among its visible tokens [0, visible(r)), -1 in the slots left over.
 //
 // One 1024-thread workgroup per row runs an exact radix select on
-// order-preserving 32-bit keys (4 passes of 8 bits, histograms per wavefront in
-// LDS so that clustered keys do not pile onto one counter), which yields the
-// exact key of the k-th largest score.  A collection pass then writes every
-// index whose key is larger (wavefront-aggregated slot reservation) and, among
-// keys equal to the threshold, the lowest indices first (an ordered block scan
-// runs only when equal keys outnumber the free slots).  Rows short enough to
-// fit are staged once into LDS so the passes do not re-read global memory.
+// order-preserving 32-bit keys.  The design keeps every step off long LDS
+// round-trip chains, which dominate at these sizes:
+//  * the row is loaded once into registers (up to 32 keys a thread; longer
+//    rows stream through registers chunk by chunk in every pass);
+//  * the first digit starts right below the bits that every key of the row
+//    shares (the common prefix of the row's largest and smallest key), so
+//    scores that sit in one binade still spread over the bins instead of
+//    piling onto one LDS address;
+//  * digits are 11 bits (2048 bins), so a continuous row is usually resolved
+//    in two passes; a pass stops the select as soon as the bin holding the
+//    k-th key is taken whole;
+//  * each pass has two barriers: after the histogram, and after the per-wave
+//    bin totals; sums, prefix sums and min/max inside a wave use DPP row
+//    operations and lane reads, not LDS shuffles;
+//  * the final pass writes the indices at ordered positions (wave-major, then
+//    key order), so the output is deterministic and, among keys equal to the
+//    threshold, the lowest indices are taken.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -24,8 +34,25 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 256;
-constexpr int kStageCap = 16384;  // keys staged in LDS (64 KiB)
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;  // two bins per thread
+constexpr int kSmallKeys = 8;           // keys per thread for rows up to 8192
+constexpr int kLargeKeys = 32;          // keys per thread (or per chunk) beyond
+
+// DPP controls (GFX9 encoding): shift right within a 16-lane row, rotate
+// within a 16-lane row.
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  // lanes whose source lies outside their row read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ uint32_t lane_of(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -33,138 +60,250 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t ballot(bool pred) { return __ballot(pred); }
-
 __device__ __forceinline__ int lane_rank(uint64_t mask) {
   // number of set bits of mask below this lane
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-template <bool STAGED>
-__device__ __forceinline__ uint32_t key_at(const float* __restrict__ row,
-                                           const uint32_t* __restrict__ staged, int i) {
-  if constexpr (STAGED) return staged[i];
-  else return order_key(row[i]);
+// Inclusive prefix sum within each 16-lane row.
+__device__ __forceinline__ uint32_t row_prefix(uint32_t x) {
+  x += dpp<kRowShr1>(x);
+  x += dpp<kRowShr2>(x);
+  x += dpp<kRowShr4>(x);
+  return x + dpp<kRowShr8>(x);
 }
 
-template <bool STAGED>
-__device__ void select_row(const float* __restrict__ row, uint32_t* staged, int n, int k,
-                           int32_t* __restrict__ out, uint32_t (*hist)[kBins],
-                           uint32_t* shared) {
+// Inclusive prefix sum over the 64 lanes; `total` receives the wave's sum.
+__device__ __forceinline__ uint32_t wave_prefix(uint32_t x, int lane, uint32_t& total) {
+  x = row_prefix(x);
+  const uint32_t r0 = lane_of(x, 15), r1 = lane_of(x, 31), r2 = lane_of(x, 47),
+                 r3 = lane_of(x, 63);
+  const int row = lane >> 4;
+  x += (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
+  total = r0 + r1 + r2 + r3;
+  return x;
+}
+
+// Sum / max / min over the 64 lanes (uniform result).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  x += dpp<kRowRor1>(x);
+  x += dpp<kRowRor2>(x);
+  x += dpp<kRowRor4>(x);
+  x += dpp<kRowRor8>(x);
+  return lane_of(x, 0) + lane_of(x, 16) + lane_of(x, 32) + lane_of(x, 48);
+}
+
+__device__ __forceinline__ uint32_t row_max(uint32_t x) {
+  x = max(x, dpp<kRowRor1>(x));
+  x = max(x, dpp<kRowRor2>(x));
+  x = max(x, dpp<kRowRor4>(x));
+  return max(x, dpp<kRowRor8>(x));
+}
+
+__device__ __forceinline__ uint32_t row_min(uint32_t x) {
+  x = min(x, dpp<kRowRor1>(x));
+  x = min(x, dpp<kRowRor2>(x));
+  x = min(x, dpp<kRowRor4>(x));
+  return min(x, dpp<kRowRor8>(x));
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = row_max(x);
+  return max(max(lane_of(x, 0), lane_of(x, 16)), max(lane_of(x, 32), lane_of(x, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  x = row_min(x);
+  return min(min(lane_of(x, 0), lane_of(x, 16)), min(lane_of(x, 32), lane_of(x, 48)));
+}
+
+__device__ __forceinline__ uint32_t high_mask(int low_bits) {
+  return low_bits >= 32 ? 0u : (~0u << low_bits);
+}
+
+struct TopkShared {
+  uint32_t hist[2][kBins];       // double-buffered histogram
+  uint32_t part[kWaves];         // per-wave bin totals / row max
+  uint32_t part2[kWaves];        // row min
+  uint32_t col_a[2][kWaves];     // per-wave counts of the final pass, by chunk parity
+  uint32_t col_e[2][kWaves];
+};
+
+// Keys of one chunk: thread (wave w, lane l) holds key j of the chunk at row
+// index chunk_base + w*64*KPT + j*64 + l (coalesced per j, wave-major order).
+template <int KPT>
+struct Chunk {
+  uint32_t key[KPT];
+  int valid;  // keys j < valid are inside the row
+
+  __device__ __forceinline__ void load(const float* __restrict__ row, int n, int64_t base) {
+    // base = chunk start + this thread's first index
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int64_t i = base + 64 * j;
+      key[j] = order_key(row[i < n ? i : n - 1]);
+    }
+    const int64_t left = (int64_t)n - base;
+    valid = left <= 0 ? 0 : (int)min<int64_t>((left + 63) / 64, KPT);
+  }
+};
+
+template <int KPT, bool STREAM>
+__device__ __forceinline__ void select_row(const float* __restrict__ row, int n, int k,
+                           int32_t* __restrict__ out, TopkShared& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  uint32_t prefix = 0, prefix_mask = 0;
-  int remaining = k;  // rank of the threshold among keys sharing the prefix
-  uint32_t eq_count = 0;
+  constexpr int kChunk = kThreads * KPT;
+  const int n_chunks = STREAM ? (n + kChunk - 1) / kChunk : 1;
+  const int64_t thread_base = (int64_t)wave * 64 * KPT + lane;
 
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kWaves * kBins; i += kThreads) (&hist[0][0])[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t key = key_at<STAGED>(row, staged, i);
-      if ((key & prefix_mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 0xFFu], 1u);
-    }
-    __syncthreads();
-    // bin totals, then the digit holding the remaining-th largest key
-    if (tid < kBins) {
-      uint32_t s = 0;
+  Chunk<KPT> ch;
+  ch.load(row, n, thread_base);
+
+  // ---- the row's largest and smallest key ----
+  uint32_t kmax = 0u, kmin = ~0u;
+  for (int c = 0; c < n_chunks; ++c) {
+    if (STREAM && c > 0) ch.load(row, n, (int64_t)c * kChunk + thread_base);
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += hist[w][tid];
-      hist[0][tid] = s;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l owns bins 4l..4l+3; suffix sums from the top bin down
-      uint32_t c[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) c[q] = hist[0][4 * lane + q];
-      const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-      // inclusive suffix scan over lanes (lane 63 = highest bins)
-      uint32_t suf = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(suf, off);
-        if (lane + off < 64) suf += o;
-      }
-      const uint32_t above_lane = suf - mine;  // keys in bins of higher lanes
-      uint32_t acc = above_lane;
-      int found = -1;
-      uint32_t above = 0, cnt = 0;
-#pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        if (found < 0 && acc + c[q] >= (uint32_t)remaining && acc < (uint32_t)remaining) {
-          found = 4 * lane + q;
-          above = acc;
-          cnt = c[q];
-        }
-        acc += c[q];
-      }
-      if (found >= 0) {
-        shared[0] = (uint32_t)found;
-        shared[1] = above;
-        shared[2] = cnt;
+    for (int j = 0; j < KPT; ++j) {
+      if (j < ch.valid) {
+        kmax = max(kmax, ch.key[j]);
+        kmin = min(kmin, ch.key[j]);
       }
     }
+  }
+  kmax = wave_max(kmax);
+  kmin = wave_min(kmin);
+  if (lane == 0) {
+    sh.part[wave] = kmax;
+    sh.part2[wave] = kmin;
+  }
+  reinterpret_cast<uint2*>(sh.hist[0])[tid] = uint2{0u, 0u};
+  __syncthreads();
+  kmax = lane_of(row_max(sh.part[lane & 15]), 0);
+  kmin = lane_of(row_min(sh.part2[lane & 15]), 0);
+
+  // bits every key shares are fixed from the start
+  int bits_left = kmax == kmin ? 0 : 32 - __builtin_clz(kmax ^ kmin);
+  uint32_t mask = high_mask(bits_left);
+  uint32_t prefix = kmax & mask;
+  int remaining = k;  // rank of the k-th key among the keys matching prefix
+  bool whole_bin = false;
+  int buf = 0;
+
+  // ---- radix passes ----
+  while (bits_left > 0) {
+    const int width = min(kDigitBits, bits_left);
+    const int shift = bits_left - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    uint32_t* h = sh.hist[buf];
+    for (int c = 0; c < n_chunks; ++c) {
+      if (STREAM) ch.load(row, n, (int64_t)c * kChunk + thread_base);
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const uint32_t key = ch.key[j];
+        if (j < ch.valid && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & dmask], 1u);
+      }
+    }
     __syncthreads();
-    const uint32_t digit = shared[0];
-    remaining -= (int)shared[1];
-    eq_count = shared[2];
+    // the other buffer was last read before this barrier: clear it for the
+    // next pass
+    reinterpret_cast<uint2*>(sh.hist[buf ^ 1])[tid] = uint2{0u, 0u};
+    const uint2 mine = reinterpret_cast<const uint2*>(h)[tid];  // bins 2*tid, 2*tid+1
+    const uint32_t wtot = wave_sum(mine.x + mine.y);
+    if (lane == 0) sh.part[wave] = wtot;
+    __syncthreads();
+
+    // every wave finds the wave span, then the bin, holding the k-th key
+    const uint32_t pv = sh.part[lane & 15];
+    const uint32_t pw = row_prefix(pv);  // every row holds waves 0..15
+    const uint32_t t16 = lane_of(pw, 15);
+    const uint32_t above_w = t16 - pw;  // keys in higher wave spans
+    const uint64_t fw = __ballot(lane < 16 && above_w < (uint32_t)remaining &&
+                                 above_w + pv >= (uint32_t)remaining);
+    const int ws = min((int)__builtin_ctzll(fw), kWaves - 1);
+    const uint32_t base_above = lane_of(above_w, ws);
+
+    const uint2 hb = reinterpret_cast<const uint2*>(h)[ws * 64 + lane];
+    const uint32_t s = hb.x + hb.y;
+    uint32_t t_w;
+    const uint32_t ps = wave_prefix(s, lane, t_w);
+    const uint32_t above_l = base_above + (t_w - ps);
+    const uint64_t fl = __ballot(above_l < (uint32_t)remaining &&
+                                 above_l + s >= (uint32_t)remaining);
+    const int ls = min((int)__builtin_ctzll(fl), 63);
+    const uint32_t a = lane_of(above_l, ls);
+    const uint32_t h0 = lane_of(hb.x, ls), h1 = lane_of(hb.y, ls);
+    const uint32_t bin_hi = 2u * (uint32_t)(ws * 64 + ls) + 1u;
+    uint32_t digit, above, cnt;
+    if (a + h1 >= (uint32_t)remaining) {
+      digit = bin_hi; above = a; cnt = h1;
+    } else {
+      digit = bin_hi - 1u; above = a + h1; cnt = h0;
+    }
+    remaining -= (int)above;
     prefix |= digit << shift;
-    prefix_mask |= 0xFFu << shift;
-    __syncthreads();
+    mask |= dmask << shift;
+    bits_left = shift;
+    buf ^= 1;
+    if (cnt == (uint32_t)remaining) {
+      whole_bin = true;  // every key of this bin is in the top k
+      break;
+    }
   }
 
-  // prefix is now the exact key of the k-th largest score; `remaining` keys
-  // equal to it are taken, `k - remaining` keys are strictly larger.
-  const uint32_t thr = prefix;
-  const bool take_all_equal = eq_count == (uint32_t)remaining;
-  if (tid == 0) shared[3] = 0u;
-  __syncthreads();
-  for (int base = 0; base < n; base += kThreads) {
-    const int i = base + tid;
-    const uint32_t key = i < n ? key_at<STAGED>(row, staged, i) : 0u;
-    const bool sel = i < n && (key > thr || (take_all_equal && key == thr));
-    const uint64_t mask = ballot(sel);
-    if (mask) {
-      uint32_t slot0 = 0;
-      if (lane == 0) slot0 = atomicAdd(&shared[3], (uint32_t)__popcll(mask));
-      slot0 = __shfl(slot0, 0);
-      const uint32_t slot = slot0 + (uint32_t)lane_rank(mask);
-      if (sel && slot < (uint32_t)k) out[slot] = i;
+  // ---- write the selection ----
+  // keys above the threshold prefix fill slots [0, k - remaining); keys equal
+  // to it take slots k - remaining + rank, rank in row order, while
+  // rank < remaining (all of them when the bin is taken whole)
+  const uint32_t first_eq = (uint32_t)(k - remaining);
+  uint32_t run_a = 0, run_e = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    if (STREAM) ch.load(row, n, (int64_t)c * kChunk + thread_base);
+    uint32_t ca = 0, ce = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t kp = ch.key[j] & mask;
+      const bool ok = j < ch.valid;
+      ca += (uint32_t)__popcll(__ballot(ok && kp > prefix));
+      ce += (uint32_t)__popcll(__ballot(ok && kp == prefix));
     }
-  }
-  if (take_all_equal) return;
-  // ties at the threshold outnumber the free slots: lowest indices first
-  __syncthreads();
-  uint32_t* wave_cnt = shared + 8;
-  int taken = 0;
-  const int first_slot = k - remaining;
-  for (int base = 0; base < n && taken < remaining; base += kThreads) {
-    const int i = base + tid;
-    const bool eq = i < n && key_at<STAGED>(row, staged, i) == thr;
-    const uint64_t mask = ballot(eq);
-    if (lane == 0) wave_cnt[wave] = (uint32_t)__popcll(mask);
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const int cw = (int)wave_cnt[w];
-      if (w < wave) before += cw;
-      total += cw;
+    if (lane == 0) {
+      sh.col_a[c & 1][wave] = ca;
+      sh.col_e[c & 1][wave] = ce;
     }
-    const int rank = taken + before + lane_rank(mask);
-    if (eq && rank < remaining) out[first_slot + rank] = i;
-    taken += total;
     __syncthreads();
+    const uint32_t pa = row_prefix(sh.col_a[c & 1][lane & 15]);
+    const uint32_t pe = row_prefix(sh.col_e[c & 1][lane & 15]);
+    const uint32_t ta = lane_of(pa, 15), te = lane_of(pe, 15);
+    uint32_t off_a = run_a + lane_of(pa, wave) - ca;  // exclusive over waves
+    uint32_t off_e = run_e + lane_of(pe, wave) - ce;
+    const int64_t base = (int64_t)c * kChunk + thread_base;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t kp = ch.key[j] & mask;
+      const bool ok = j < ch.valid;
+      const uint64_t ma = __ballot(ok && kp > prefix);
+      const uint64_t me = __ballot(ok && kp == prefix);
+      const int32_t idx = (int32_t)(base + 64 * j);
+      if (ok && kp > prefix) out[off_a + (uint32_t)lane_rank(ma)] = idx;
+      if (ok && kp == prefix) {
+        const uint32_t rank = off_e + (uint32_t)lane_rank(me);
+        if (rank < (uint32_t)remaining) out[first_eq + rank] = idx;
+      }
+      off_a += (uint32_t)__popcll(ma);
+      off_e += (uint32_t)__popcll(me);
+    }
+    run_a += ta;
+    run_e += te;
   }
+  (void)whole_bin;
 }
 
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
-  __shared__ uint32_t hist[kWaves][kBins];
-  __shared__ uint32_t shared[32];
-  __shared__ uint32_t staged[kStageCap];
+  __shared__ TopkShared sh;
 
   const int r = blockIdx.x;
   const int b = r / p.next_n;
@@ -180,13 +319,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
     return;
   }
-  if (n <= kStageCap) {
-    for (int i = threadIdx.x; i < n; i += kThreads) staged[i] = order_key(row[i]);
-    __syncthreads();
-    select_row<true>(row, staged, n, k, out, hist, shared);
-  } else {
-    select_row<false>(row, staged, n, k, out, hist, shared);
-  }
+  if (n <= kThreads * kSmallKeys)
+    select_row<kSmallKeys, false>(row, n, k, out, sh);
+  else if (n <= kThreads * kLargeKeys)
+    select_row<kLargeKeys, false>(row, n, k, out, sh);
+  else
+    select_row<kLargeKeys, true>(row, n, k, out, sh);
 }
 
 }  // namespace

@@ -207,7 +207,8 @@ def test_config5_long_context(gpu_lib):
 def test_topk_synthetic_rows(gpu_lib, ties):
     """The top-k alone on seeded score rows: exact sets (same fp32 inputs on both
     sides), lowest indices among equal scores, every row length class."""
-    lens = [0, 1, 100, 2047, 2048, 2049, 4000, 16384, 16385, 40000, 131072]
+    lens = [0, 1, 100, 2047, 2048, 2049, 4000, 8192, 8193, 16384, 16385, 32768, 32769,
+            40000, 131072]
     width = max(lens)
     dense = synth.make_logit_rows(len(lens), width, lens, seed=5, ties=ties)
     ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
@@ -218,6 +219,46 @@ def test_topk_synthetic_rows(gpu_lib, ties):
         gpu_lib.topk_per_row(logits, ctx, k, idx, next_n=1)
         torch.cuda.synchronize()
         want = oracle.topk_per_row([dense[r, :n] for r, n in enumerate(lens)], k)
+        got = idx.cpu().numpy()
+        for r, n in enumerate(lens):
+            m = min(k, n)
+            assert sorted(got[r, :m].tolist()) == sorted(want[r, :m].tolist()), f"row {r} n={n} k={k}"
+            assert np.all(got[r, m:] == -1)
+
+
+def test_topk_special_rows(gpu_lib):
+    """Rows the score distribution never produces but the op accepts: one value
+    repeated (every key ties), both zeros (equal scores), infinities, subnormals
+    and both signs, at lengths on each side of the register-resident limits."""
+    rng = np.random.default_rng(11)
+    rows = []
+    for n in (3000, 9000, 40000):
+        rows.append(np.full(n, 1.5, dtype=np.float32))
+        z = np.where(rng.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        z[rng.choice(n, 50, replace=False)] = 1.0
+        rows.append(z)
+        mix = rng.standard_normal(n).astype(np.float32) * np.float32(1e30)
+        pick = rng.choice(n, 40, replace=False)
+        mix[pick[:10]] = np.inf
+        mix[pick[10:20]] = -np.inf
+        mix[pick[20:30]] = np.float32(1e-45)
+        mix[pick[30:40]] = np.float32(-1e-45)
+        rows.append(mix)
+        two = np.where(rng.random(n) < 0.7, np.float32(-2.0), np.float32(3.0)).astype(np.float32)
+        rows.append(two)
+    lens = [len(r) for r in rows]
+    width = max(lens)
+    dense = np.full((len(rows), width), -np.inf, dtype=np.float32)
+    for i, r in enumerate(rows):
+        dense[i, : len(r)] = r
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    logits = torch.from_numpy(dense).cuda()
+    for k in (1, 100, 2048):
+        idx = torch.full((len(rows), k), -7, dtype=torch.int32, device="cuda")
+        say(f"[gpu] topk_per_row special rows k={k}")
+        gpu_lib.topk_per_row(logits, ctx, k, idx, next_n=1)
+        torch.cuda.synchronize()
+        want = oracle.topk_per_row(rows, k)
         got = idx.cpu().numpy()
         for r, n in enumerate(lens):
             m = min(k, n)
@@ -238,3 +279,31 @@ def test_short_rows_meet_row_tolerance(gpu_lib, heads):
     out = run_logits(gpu_lib, wl, d)
     worst = check_rows(wl, out, oracle_rows(wl))
     say(f"short rows H={heads}: worst rel err {worst:.3e}")
+
+
+def test_graph_replay_matches_eager(gpu_lib, cfg2):
+    """The step captured as a HIP graph (as the benchmark replays it) gives the
+    eager results on every replay, with eager work and syncs in between."""
+    wl = cfg2
+    d = upload(wl)
+    out_e = run_logits(gpu_lib, wl, d, label="eager")
+    idx_e = topk_gpu(gpu_lib, wl, out_e, ctx=d["ctx"])
+    out = new_out(wl.rows, wl.out_row_stride)
+    idx = torch.full((wl.rows, wl.topk), -7, dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    say("[gpu] capture logits + topk graph")
+    with torch.cuda.graph(g):
+        gpu_lib.paged_mqa_logits(d["q"], d["kv"], d["w"], d["ctx"], d["tab"], wl.page_size,
+                                 wl.next_n, out)
+        gpu_lib.topk_per_row(out, d["ctx"], wl.topk, idx, next_n=wl.next_n)
+    want = np.sort(idx_e.cpu().numpy(), axis=1)
+    for rep in range(4):
+        out.view(torch.int32).fill_(SENTINEL_BITS)
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        say(f"[gpu] graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), out_e.view(torch.int32)), f"replay {rep}"
+        assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), want), f"replay {rep}"
+        run_logits(gpu_lib, wl, d, label="eager between replays")
