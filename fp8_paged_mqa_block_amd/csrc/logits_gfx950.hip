@@ -47,9 +47,9 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "pmqa_internal.h"
+#include "wave_ops.h"
 
 namespace pmqa {
 namespace {
@@ -129,91 +129,101 @@ __device__ __forceinline__ int n_iters(int ctx, int max_tokens) {
   return (c + kIterTokens - 1) / kIterTokens;
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// The context lengths of 64 consecutive requests, one per lane, so that the
-// wave can step from request to request without a memory round trip inside
-// its pipeline (a load there would make the compiler drain every in-flight
-// gather).  Reloaded, with an explicit full wait, when a wave's run crosses
-// into the next 64 requests.
-struct CtxWindow {
-  int c0;   // first request held
-  int len;  // lane i: context length of request c0 + i (0 past the batch)
+__device__ __forceinline__ uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1u) / b; }
+
+// One wave's share of the work: iterations [it0, it0 + n_it) of request b
+// (all wave-uniform).  A run never crosses into another request, so the wave
+// loads its q rows once.
+struct Run {
+  int b, ctx, ctx_eff, it0, n_it;
 };
 
-__device__ __forceinline__ void load_window(const LogitsParams& p, int c0, int lane, CtxWindow& w) {
-  w.c0 = c0;
-  w.len = c0 + lane < p.batch ? max(p.ctx[c0 + lane], 0) : 0;
-  __builtin_amdgcn_s_waitcnt(0);
+// Iterations of request c0 + lane (0 past the batch), and its context length.
+__device__ __forceinline__ int lane_iters(const LogitsParams& p, int c0, int lane, int& ctx) {
+  const int b = c0 + lane;
+  ctx = b < p.batch ? max(p.ctx[b], 0) : 0;
+  return n_iters(ctx, p.max_tokens);
 }
 
-// Position in the iteration list: request b, iteration it, and b's length
-// (all wave-uniform).
-struct Cursor {
-  int b, it, ctx, ctx_eff;
-};
-
-// Cursor at iteration it of request b.  Requests inside the window come from
-// its lanes; one outside it (the page-id walk runs ahead of the gather walk
-// and may already have moved the window on) is read from memory, with an
-// explicit full wait.
-__device__ __forceinline__ Cursor cursor_at(const LogitsParams& p, const CtxWindow& w, int b,
-                                            int it) {
-  Cursor c;
-  c.b = b;
-  c.it = it;
-  if ((unsigned)(b - w.c0) < 64u) {
-    c.ctx = __builtin_amdgcn_readlane(w.len, b - w.c0);
-  } else {
-    c.ctx = uniform(max(p.ctx[b], 0));
-    __builtin_amdgcn_s_waitcnt(0);
+// Runs needed when no run is longer than P iterations: sum over the batch of
+// ceil(n_b / P).
+__device__ uint64_t runs_for(const LogitsParams& p, int lane, uint32_t n_first, uint32_t P) {
+  uint64_t runs = wave_sum(ceil_div(n_first, P));
+  for (int c0 = 64; c0 < p.batch; c0 += 64) {
+    int ctx;
+    runs += wave_sum(ceil_div((uint32_t)lane_iters(p, c0, lane, ctx), P));
   }
-  c.ctx_eff = min(c.ctx, p.max_tokens);
-  return c;
+  return runs;
 }
 
-// Next iteration in the list (skips requests with nothing to score).  Only
-// called while iterations remain, so a non-empty request always follows.
-__device__ __forceinline__ Cursor advance(const LogitsParams& p, CtxWindow& w, int lane,
-                                          Cursor c) {
-  if ((c.it + 1) * kIterTokens < c.ctx_eff) {
-    ++c.it;
-    return c;
+// The work split.  Every request b is cut into ceil(n_b / P) runs of nearly
+// equal length (n_b iterations), with P the smallest length for which all the
+// runs fit in the n_slices units the grid provides (one run per request
+// always fits: the host makes n_slices >= batch).  Unit u takes the u-th run
+// in request order; units past the last run have nothing to do.  Each wave
+// computes the split itself from the context lengths, so the host never reads
+// them.
+__device__ bool find_run(const LogitsParams& p, int unit, int lane, Run& run) {
+  int ctx0;
+  const uint32_t n0 = (uint32_t)lane_iters(p, 0, lane, ctx0);
+  uint64_t total = wave_sum(n0);
+  uint32_t nmax = wave_max(n0);
+  for (int c0 = 64; c0 < p.batch; c0 += 64) {
+    int ctx;
+    const uint32_t n = (uint32_t)lane_iters(p, c0, lane, ctx);
+    total += wave_sum(n);
+    nmax = max(nmax, wave_max(n));
   }
-  int b = c.b;
-  Cursor n;
-  do {
-    ++b;
-    if (b - w.c0 == 64) load_window(p, b, lane, w);  // first step past the window
-    n = cursor_at(p, w, b, 0);
-  } while (n.ctx_eff == 0 && b + 1 < p.batch);
-  return n;
+  if (total == 0) return false;
+  const uint32_t slices = (uint32_t)p.n_slices;
+  uint32_t P = (uint32_t)((total + slices - 1) / slices);
+  if (runs_for(p, lane, n0, P) > slices) {
+    // runs_for(lo) > slices >= runs_for(hi): bisect for the smallest fit
+    uint32_t lo = P, hi = nmax;
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      if (runs_for(p, lane, n0, mid) <= slices) hi = mid;
+      else lo = mid;
+    }
+    P = hi;
+  }
+  // locate unit: the request whose runs cover it
+  uint32_t before = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+    int ctx = ctx0;
+    const uint32_t n = c0 == 0 ? n0 : (uint32_t)lane_iters(p, c0, lane, ctx);
+    const uint32_t c = ceil_div(n, P);
+    uint32_t chunk_runs;
+    const uint32_t incl = wave_prefix(c, lane, chunk_runs);
+    if (before + chunk_runs > (uint32_t)unit) {
+      const uint64_t past = __ballot(before + incl > (uint32_t)unit);
+      const int f = uniform(__builtin_ctzll(past));
+      const uint32_t c_f = lane_of(c, f), n_f = lane_of(n, f);
+      const uint32_t i = (uint32_t)unit - (before + lane_of(incl, f) - c_f);
+      run.b = c0 + f;
+      run.ctx = (int)lane_of((uint32_t)ctx, f);
+      run.ctx_eff = min(run.ctx, p.max_tokens);
+      run.it0 = (int)((uint64_t)n_f * i / c_f);
+      run.n_it = (int)((uint64_t)n_f * (i + 1u) / c_f) - run.it0;
+      return true;
+    }
+    before += chunk_runs;
+  }
+  return false;
 }
 
 template <int H, int JW>
 struct QRegs {
   v8i qa[JW][H / 16];
   v4f wv[JW][H / 16];
-  int b;  // request whose q rows are loaded
 };
 
-// Load q rows and weights of request b and wait for them (an explicit full
-// wait, so no later code needs a compiler-inserted one).
+// Load the q rows and weights of request b.  The caller ends the loads with
+// an explicit full wait the compiler knows about, so no later code needs a
+// compiler-inserted one (which, with LDS-bound loads in flight, would be a
+// full drain inside the pipeline).
 template <int H, int JW>
 __device__ __forceinline__ void load_q(const LogitsParams& p, int b, int j0, int m, int kq,
                                        QRegs<H, JW>& qr) {
@@ -230,16 +240,14 @@ __device__ __forceinline__ void load_q(const LogitsParams& p, int b, int j0, int
       qr.wv[jj][ht] = *reinterpret_cast<const v4f*>(wrow + ht * 16 + kq * 4);
     }
   }
-  qr.b = b;
-  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Page ids of an iteration, gathered into LDS by one 4-byte-per-lane load:
 // lanes 2i and 2i+1 move the two halves of the iteration's i-th page id.
 // Only ids inside the context are read (at most 8 pages per iteration).
-__device__ __forceinline__ void issue_ids(const LogitsParams& p, const Cursor& c, int lane,
+__device__ __forceinline__ void issue_ids(const LogitsParams& p, const Run& c, int it, int lane,
                                           int64_t* ids_slot) {
-  const int t0 = c.it * kIterTokens;
+  const int t0 = it * kIterTokens;
   const int lp = p.log2_page;
   const int p_first = t0 >> lp;
   const int n_pg = ((min(t0 + kIterTokens, c.ctx_eff) - 1) >> lp) - p_first + 1;
@@ -292,11 +300,13 @@ __device__ __forceinline__ GatherPages read_pages(const int64_t* ids_slot, int l
 // lane for the values (8 tokens per instruction; a page holds at least 8
 // tokens, so an instruction's tokens share one page) and one of 4 bytes per
 // lane for the scales (token = lane).  Exactly kGatherLoads vector memory
-// instructions are issued on every call: lanes past the context fetch the
-// pool's first record instead, and their results are never stored.
-__device__ __forceinline__ void issue_gather(const LogitsParams& p, const Cursor& c,
+// instructions are issued on every call: lanes at or past `limit` (the
+// context, or 0 for a placeholder gather that only keeps the instruction count
+// fixed) fetch the pool's first record instead and never read their ids, and
+// their results are never stored.
+__device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int limit,
                                              const int64_t* ids_slot, int lane, uint8_t* slot) {
-  const int t0 = c.it * kIterTokens;
+  const int t0 = it * kIterTokens;
   const int in_page_mask = p.page_size - 1;
   const int sub = lane >> 3;                 // token within the instruction's 8
   const int chunk = (lane & 7) ^ sub;        // swizzled 16-byte chunk this lane moves
@@ -304,14 +314,14 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, const Cursor
 #pragma unroll
   for (int i = 0; i < kDmaPerIter; ++i) {
     const int t = t0 + 8 * i + sub;
-    const int64_t off = t < c.ctx_eff ? pg.group[i] * p.page_bytes +
+    const int64_t off = t < limit ? pg.group[i] * p.page_bytes +
                                             (int32_t)((t & in_page_mask) * kRecordBytes) + 16 * chunk
                                       : (int64_t)(16 * chunk);
     __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * 1024), 16, 0, 0);
   }
   const int t = t0 + lane;
   const int64_t soff =
-      t < c.ctx_eff ? pg.lane * p.page_bytes + (int32_t)((t & in_page_mask) * kRecordBytes) : 0;
+      t < limit ? pg.lane * p.page_bytes + (int32_t)((t & in_page_mask) * kRecordBytes) : 0;
   __builtin_amdgcn_global_load_lds(p.kv + soff + kHeadDim, LDS_PTR(slot + kSlotValueBytes), 4,
                                    0, 0);
 }
@@ -337,32 +347,19 @@ __device__ __forceinline__ float sum_rows(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Score one iteration (64 tokens x the wave's rows) from its LDS slot and
+// Score one iteration (64 tokens x the wave's rows) from its slot operands and
 // store it.  FACTORED: every scale of the iteration is >= 0, so
 // relu(s * x) = s * relu(x) and the scale multiplies the head-weighted sum once
 // per token instead of once per head (2 VALU operations per MFMA output
 // instead of 3); otherwise the literal form runs.
 template <int H, int JW, bool EXACT, bool FACTORED>
-__device__ __forceinline__ void score_iteration(const LogitsParams& p, const Cursor& c, int j0,
+__device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run& c, int it, int j0,
                                                 int lane, const QRegs<H, JW>& qr,
-                                                const uint8_t* slot) {
+                                                const v8i (&kb)[kTilesPerIter],
+                                                const float (&sc)[kTilesPerIter]) {
   constexpr int HT = H / 16;
-  const int m = lane & 15, kq = lane >> 4;
-  const float* scales = reinterpret_cast<const float*>(slot + kSlotValueBytes);
-  const int t0 = c.it * kIterTokens;
-  // B operands and scales of the 4 tiles
-  v8i kb[kTilesPerIter];
-  float sc[kTilesPerIter];
-#pragma unroll
-  for (int tile = 0; tile < kTilesPerIter; ++tile) {
-    const int tl = tile * kTile + m;
-    const uint8_t* row = slot + tl * 128;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(row + 16 * ((2 * kq) ^ (m & 7)));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 16 * ((2 * kq + 1) ^ (m & 7)));
-    kb[tile][0] = lo[0]; kb[tile][1] = lo[1]; kb[tile][2] = lo[2]; kb[tile][3] = lo[3];
-    kb[tile][4] = hi[0]; kb[tile][5] = hi[1]; kb[tile][6] = hi[2]; kb[tile][7] = hi[3];
-    sc[tile] = t0 + tl < c.ctx_eff ? scales[tl] : 0.f;  // tokens past the context: 0
-  }
+  const int kq = lane >> 4;
+  const int t0 = it * kIterTokens;
   float keep[JW];
 #pragma unroll
   for (int jj = 0; jj < JW; ++jj) keep[jj] = 0.f;
@@ -413,36 +410,96 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Cur
   }
 }
 
+// The iteration's operands from its LDS slot: each lane's two 16-byte halves
+// of its token's 32-byte B operand per tile (chunk c of local token t sits at
+// t*128 + 16*(c ^ (t & 7))) and the scales of those 4 tokens.  Inline
+// assembly with its own LDS wait on purpose: the compiler cannot tell which
+// in-flight LDS-bound loads a plain LDS read could alias and would drain every
+// one of them first (the whole ring), while the explicit vector-memory wait
+// before this read already proves this slot has landed.
+struct SlotOperands {
+  v8i kb[kTilesPerIter];
+  float sc[kTilesPerIter];
+};
+
+__device__ __forceinline__ SlotOperands read_slot(const uint8_t* slot, int lane) {
+  static_assert(kTilesPerIter == 4 && kTile * 128 == 2048, "offsets below assume 4 tiles of 16 tokens");
+  const int m = lane & 15, kq = lane >> 4;
+  const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)slot);
+  // tile t's addresses are tile 0's plus t * 2048 (values) or t * 64 (scales)
+  const uint32_t alo = base + (uint32_t)m * 128u + 16u * (uint32_t)((2 * kq) ^ (m & 7));
+  const uint32_t ahi = base + (uint32_t)m * 128u + 16u * (uint32_t)((2 * kq + 1) ^ (m & 7));
+  const uint32_t as = base + (uint32_t)kSlotValueBytes + 4u * (uint32_t)m;
+  u32x4 lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
+  SlotOperands r;
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %12 offset:2048\n\t"
+      "ds_read_b128 %3, %13 offset:2048\n\t"
+      "ds_read_b128 %4, %12 offset:4096\n\t"
+      "ds_read_b128 %5, %13 offset:4096\n\t"
+      "ds_read_b128 %6, %12 offset:6144\n\t"
+      "ds_read_b128 %7, %13 offset:6144\n\t"
+      "ds_read_b32 %8, %14\n\t"
+      "ds_read_b32 %9, %14 offset:64\n\t"
+      "ds_read_b32 %10, %14 offset:128\n\t"
+      "ds_read_b32 %11, %14 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo0), "=&v"(hi0), "=&v"(lo1), "=&v"(hi1), "=&v"(lo2), "=&v"(hi2), "=&v"(lo3),
+        "=&v"(hi3), "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3])
+      : "v"(alo), "v"(ahi), "v"(as)
+      : "memory");
+  const u32x4 lo[kTilesPerIter] = {lo0, lo1, lo2, lo3};
+  const u32x4 hi[kTilesPerIter] = {hi0, hi1, hi2, hi3};
+#pragma unroll
+  for (int tile = 0; tile < kTilesPerIter; ++tile) {
+    r.kb[tile][0] = lo[tile][0]; r.kb[tile][1] = lo[tile][1];
+    r.kb[tile][2] = lo[tile][2]; r.kb[tile][3] = lo[tile][3];
+    r.kb[tile][4] = hi[tile][0]; r.kb[tile][5] = hi[tile][1];
+    r.kb[tile][6] = hi[tile][2]; r.kb[tile][7] = hi[tile][3];
+  }
+  return r;
+}
+
 template <int H, int JW>
-__device__ __forceinline__ void score(const LogitsParams& p, const Cursor& c, int j0, int lane,
+__device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int it, int j0, int lane,
                                       const QRegs<H, JW>& qr, const uint8_t* slot) {
   // the wave's first row sees the fewest tokens
   const int min_vis = min(max(c.ctx - p.next_n + j0 + 1, 0), c.ctx);
-  // scales of the iteration's tokens (one per lane), past the context: 0
-  const float* scales = reinterpret_cast<const float*>(slot + kSlotValueBytes);
-  const float s = c.it * kIterTokens + lane < c.ctx_eff ? scales[lane] : 0.f;
-  const bool factored = __ballot(!(s >= 0.f)) == 0;  // NaN also takes the literal form
+  SlotOperands op = read_slot(slot, lane);
+  const int t0 = it * kIterTokens + (lane & 15);
+  bool bad = false;
+#pragma unroll
+  for (int tile = 0; tile < kTilesPerIter; ++tile) {
+    // tokens past the context: scale 0, never stored
+    op.sc[tile] = t0 + tile * kTile < c.ctx_eff ? op.sc[tile] : 0.f;
+    bad |= !(op.sc[tile] >= 0.f);  // NaN also takes the literal form
+  }
+  const bool factored = __ballot(bad) == 0;
   if (min_vis < kExactRows) {
-    if (factored) score_iteration<H, JW, true, true>(p, c, j0, lane, qr, slot);
-    else score_iteration<H, JW, true, false>(p, c, j0, lane, qr, slot);
+    if (factored) score_iteration<H, JW, true, true>(p, c, it, j0, lane, qr, op.kb, op.sc);
+    else score_iteration<H, JW, true, false>(p, c, it, j0, lane, qr, op.kb, op.sc);
   } else {
-    if (factored) score_iteration<H, JW, false, true>(p, c, j0, lane, qr, slot);
-    else score_iteration<H, JW, false, false>(p, c, j0, lane, qr, slot);
+    if (factored) score_iteration<H, JW, false, true>(p, c, it, j0, lane, qr, op.kb, op.sc);
+    else score_iteration<H, JW, false, false>(p, c, it, j0, lane, qr, op.kb, op.sc);
   }
 }
 
 // H heads; JW next_n rows per wave; WAVES waves per workgroup (one workgroup
 // per CU); RING iterations in flight per wave.
 //
-// Pipeline of one wave (refill(j) = page ids of iteration j+2R, then the gather
-// of iteration j+R; R = RING):
-//   prologue: ids of iterations 0..R-1 and the q rows (waited for),
-//             refill(-R) .. refill(-1)
+// Pipeline of one wave over its run of n iterations (refill(j) = page ids of
+// iteration j+2R, then the gather of iteration j+R; R = RING):
+//   prologue: ids of iterations 0..R-1 and the q rows (waited for), then
+//             refill(-R) .. refill(-1) -- always R gathers, placeholders past
+//             the run, so that the count of gathers in flight is fixed (one
+//             slot: the q rows are loaded after the gather instead)
 //   loop k:   wait for gather k; score k from its slot; refill(k)
-// The ids refill(k) uses (those of iteration k+R) were issued by refill(k-R)
-// before the gather of k, so "gather k has landed" (the vector memory counter
-// drains in order) also proves they have landed.  Ids of iteration j live in
-// id slot j % 2R, values in ring slot j % R.
+// The ids refill(k) uses (those of iteration k+R) were issued by
+// refill(k-R) before the gather of k, so "gather k has landed" (the vector
+// memory counter drains in order) also proves they have landed.  Ids of
+// iteration j live in id slot j % 2R, values in ring slot j % R.
 template <int H, int JW, int WAVES, int RING>
 __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][RING][kSlotBytes];
@@ -450,128 +507,81 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 15;   // token within a tile (B column / A row)
   const int kq = lane >> 4;  // 32-byte quarter of the head dimension
-  const int wl = threadIdx.x >> 6;
+  const int wl = uniform(threadIdx.x >> 6);
   const uint32_t nwg = gridDim.x;  // a multiple of 8
   const uint32_t wg = (blockIdx.x & 7u) * (nwg >> 3) + (blockIdx.x >> 3);
-  const uint32_t wave = wg * WAVES + wl;
+  // units are dealt wave-major over the workgroups, so that when fewer units
+  // than waves have work every CU still gets its share
+  const uint32_t wave = (uint32_t)wl * nwg + wg;
   if (wave >= (uint32_t)p.n_slices * (uint32_t)p.n_rgroups) return;
-  const int slice = (int)(wave / (uint32_t)p.n_rgroups);
+  const int unit = (int)(wave / (uint32_t)p.n_rgroups);
   const int j0 = (int)(wave % (uint32_t)p.n_rgroups) * JW;
 
-  // this slice's share [lo, hi) of the iteration list, and the 64 context
-  // lengths around its start
-  CtxWindow win;
-  Cursor first;
-  int64_t lo, hi;
-  if (p.batch <= 64) {
-    // one load: the whole batch is the window
-    win.c0 = 0;
-    win.len = lane < p.batch ? max(p.ctx[lane], 0) : 0;
-    const int n = n_iters(win.len, p.max_tokens);
-    const int incl = wave_incl_scan(n, lane);
-    const int64_t total = uniform(__shfl(incl, 63));
-    lo = total * slice / p.n_slices;
-    hi = total * (slice + 1) / p.n_slices;
-    if (lo >= hi) return;
-    const uint64_t past = __ballot(incl > lo);
-    const int f = uniform(__builtin_ctzll(past));
-    const int incl_f = uniform(__shfl(incl, f));
-    const int n_f = uniform(__shfl(n, f));
-    first = cursor_at(p, win, f, (int)(lo - (incl_f - n_f)));
-  } else {
-    int64_t total = 0;
-    for (int c0 = 0; c0 < p.batch; c0 += 64) {
-      const int b = c0 + lane;
-      total += uniform(wave_sum(b < p.batch ? n_iters(p.ctx[b], p.max_tokens) : 0));
-    }
-    lo = total * slice / p.n_slices;
-    hi = total * (slice + 1) / p.n_slices;
-    if (lo >= hi) return;
-    int64_t before = 0;
-    for (int c0 = 0;; c0 += 64) {
-      const int b = c0 + lane;
-      const int n = b < p.batch ? n_iters(p.ctx[b], p.max_tokens) : 0;
-      const int incl = wave_incl_scan(n, lane);
-      const int chunk = uniform(__shfl(incl, 63));
-      if (before + chunk > lo) {
-        const uint64_t past = __ballot(before + incl > lo);
-        const int f = uniform(__builtin_ctzll(past));
-        const int incl_f = uniform(__shfl(incl, f));
-        const int n_f = uniform(__shfl(n, f));
-        load_window(p, c0 + f, lane, win);
-        first = cursor_at(p, win, c0 + f, (int)(lo - (before + incl_f - n_f)));
-        break;
-      }
-      before += chunk;
-    }
-  }
-  const int n_it = (int)(hi - lo);
+  Run run;
+  if (!find_run(p, unit, lane, run)) return;
+  const int n_it = run.n_it;
   uint8_t* my_ring = &ring[wl][0][0];
   int64_t* my_ids = &ids[wl][0][0];
 
-  // prologue: ids of the first RING iterations and the q rows, waited for together
-  Cursor cs[RING];  // iteration scored from ring slot s: k with k % RING == s
-  cs[0] = first;
-#pragma unroll
-  for (int s = 1; s < RING; ++s) cs[s] = s < n_it ? advance(p, win, lane, cs[s - 1]) : cs[s - 1];
+  // prologue
 #pragma unroll
   for (int s = 0; s < RING; ++s)
-    if (s < n_it) issue_ids(p, cs[s], lane, my_ids + s * kDmaPerIter);
+    if (s < n_it) issue_ids(p, run, run.it0 + s, lane, my_ids + s * kDmaPerIter);
   QRegs<H, JW> qr;
-  load_q<H, JW>(p, first.b, j0, m, kq, qr);  // ends with a full wait
-  Cursor ahead = cs[RING - 1];  // last iteration whose ids were issued
+  if constexpr (RING > 1) load_q<H, JW>(p, run.b, j0, m, kq, qr);
+  __builtin_amdgcn_s_waitcnt(0);  // ids of the first R iterations (and q)
   int n_ids = min(n_it, RING);  // iterations whose ids were issued
 #pragma unroll
   for (int s = 0; s < RING; ++s) {
-    if (s < n_it) {
-      // refill(s - R): ids of iteration s + R, then the gather of s
-      if (n_ids < n_it) {
-        ahead = advance(p, win, lane, ahead);
-        issue_ids(p, ahead, lane, my_ids + (n_ids % (2 * RING)) * kDmaPerIter);
-        ++n_ids;
-      }
-      issue_gather(p, cs[s], my_ids + s * kDmaPerIter, lane, my_ring + s * kSlotBytes);
+    if (n_ids < n_it) {
+      issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kDmaPerIter);
+      ++n_ids;
     }
+    issue_gather(p, run.it0 + s, s < n_it ? run.ctx_eff : 0, my_ids + s * kDmaPerIter, lane,
+                 my_ring + s * kSlotBytes);
   }
-
+  // with one slot, the first score waits for every load anyway: q behind the
+  // first gather keeps its latency off the path to the K stream
+  if constexpr (RING == 1) load_q<H, JW>(p, run.b, j0, m, kq, qr);
+  const int n_span = max(n_it, RING);
   for (int k0 = 0; k0 < n_it; k0 += RING) {
 #pragma unroll
     for (int s = 0; s < RING; ++s) {
       const int k = k0 + s;
       if (k >= n_it) break;
-      // the gathers of iterations k+1 .. min(k+R-1, n_it-1) were issued after
-      // this one's, kGatherLoads instructions each (page-id loads and stores
-      // issued in between only add to the count): once at most that many are
-      // outstanding, iteration k's data has landed in its slot
-      wait_vm(kGatherLoads * min(RING - 1, n_it - 1 - k));
-      if (cs[s].b != qr.b) load_q<H, JW>(p, cs[s].b, j0, m, kq, qr);
-      score<H, JW>(p, cs[s], j0, lane, qr, my_ring + s * kSlotBytes);
+      // the gathers issued after this one's (kGatherLoads instructions each;
+      // page-id loads and stores issued in between only add to the count):
+      // once at most that many are outstanding, iteration k's data has landed
+      wait_vm(kGatherLoads * min(RING - 1, n_span - 1 - k));
+      score<H, JW>(p, run, run.it0 + k, j0, lane, qr, my_ring + s * kSlotBytes);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot reads done before refill
       if (k + RING < n_it) {
         // refill(k): ids of iteration k + 2R, then the gather of k + R
-        const Cursor g = advance(p, win, lane, cs[(s + RING - 1) % RING]);
         if (n_ids < n_it) {
-          ahead = advance(p, win, lane, ahead);
-          issue_ids(p, ahead, lane, my_ids + (n_ids % (2 * RING)) * kDmaPerIter);
+          issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kDmaPerIter);
           ++n_ids;
         }
-        cs[s] = g;
-        issue_gather(p, g, my_ids + ((k + RING) % (2 * RING)) * kDmaPerIter, lane,
+        issue_gather(p, run.it0 + k + RING, run.ctx_eff,
+                     my_ids + ((k + RING) % (2 * RING)) * kDmaPerIter, lane,
                      my_ring + s * kSlotBytes);
       }
     }
   }
 }
 
-// Launch geometry per instantiation: wave units of at most 64 q rows run two
-// waves per SIMD (8 per workgroup, 2 iterations in flight each) so that one
-// wave's matrix work overlaps the other's memory stalls; larger ones need the
-// registers of a whole SIMD and run 4 waves per workgroup with 4 in flight.
+// Launch geometry per instantiation.  Wave units of at most 64 q rows (and at
+// most 3 next_n rows, whose partial sums also take registers) run 9 waves per
+// workgroup (2-3 per SIMD, so that one wave's matrix work overlaps another's
+// memory stalls) with one iteration in flight each: measured on the decode
+// shape, a second slot per wave made waves stall on issuing its gather behind
+// the saturated memory pipeline before scoring the first, which cost more than
+// the prefetch gained.  Larger units need the registers of a whole SIMD and run
+// 4 waves with 4 iterations in flight.
 template <int H, int JW>
 struct Geometry {
-  static constexpr bool kSmall = H * JW <= 64;
-  static constexpr int kWaves = kSmall ? 8 : 4;
-  static constexpr int kRingDepth = kSmall ? 2 : 4;
+  static constexpr bool kSmall = H * JW <= 64 && JW <= 3;
+  static constexpr int kWaves = kSmall ? 9 : 4;
+  static constexpr int kRingDepth = kSmall ? 1 : 4;
 };
 
 template <int H, int JW>
@@ -634,7 +644,6 @@ LogitsShape logits_shape(int heads, int next_n) {
     case 128: per_cu = waves_per_cu<128>(sh.rows_per_wave); break;
   }
   sh.target_waves = 256 * per_cu;
-  if (const char* e = getenv("PMQA_LOGITS_WAVES")) sh.target_waves = atoi(e);
   return sh;
 }
 

@@ -84,12 +84,15 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
   p.max_tokens = (int32_t)max_tokens;
   const pmqa::LogitsShape sh = pmqa::logits_shape(num_heads, next_n);
   const int64_t n_rgroups = (next_n + sh.rows_per_wave - 1) / sh.rows_per_wave;
-  // the persistent grid: enough runs to fill the chip, never more than the
-  // iterations the contexts could hold
+  // the grid's work units: enough to fill the chip, and at least 4 per request
+  // so that the device-side split (runs never cross requests) stays balanced
+  // when requests are long and few units are resident at once; never more
+  // than the iterations the contexts could hold, never fewer than the batch
   const int64_t max_iters = (int64_t)batch * ((max_tokens + sh.iter_tokens - 1) / sh.iter_tokens);
   int64_t n_slices = sh.target_waves / n_rgroups;
-  if (n_slices < 1) n_slices = 1;
+  if (n_slices < 4 * (int64_t)batch) n_slices = 4 * (int64_t)batch;
   if (n_slices > max_iters) n_slices = max_iters;
+  if (n_slices > INT32_MAX / n_rgroups) n_slices = INT32_MAX / n_rgroups;  // still >= batch
   p.n_slices = (int32_t)n_slices;
   p.n_rgroups = (int32_t)n_rgroups;
   if (!is_pow2(page_size)) return PMQA_ERR_SHAPE;

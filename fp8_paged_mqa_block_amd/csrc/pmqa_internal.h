@@ -26,7 +26,7 @@ struct LogitsParams {
   int32_t page_size;
   int32_t log2_page;
   int32_t max_tokens;      // min(table_stride*page_size, out_stride), clamped to int32
-  int32_t n_slices;        // runs of iterations the persistent grid splits the work into
+  int32_t n_slices;        // work units of the grid (>= batch); each takes one run
   int32_t n_rgroups;       // waves per run splitting the next_n rows
 };
 
