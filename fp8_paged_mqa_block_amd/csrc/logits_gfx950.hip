@@ -63,10 +63,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kTile = 16;                 // tokens per MFMA tile (N)
 constexpr int kTilesPerIter = 4;          // 64 tokens: one per lane at store time
 constexpr int kIterTokens = kTile * kTilesPerIter;
-constexpr int kSlotValueBytes = kIterTokens * 128;     // K values of one iteration
-constexpr int kSlotBytes = kSlotValueBytes + kIterTokens * 4;  // + its fp32 scales
-constexpr int kDmaPerIter = kIterTokens / 8;   // 8 tokens per 64-lane 16-byte load
-constexpr int kGatherLoads = kDmaPerIter + 1;  // vector memory instructions per gather
+// In LDS a token record takes 9 chunks of 16 bytes (144 bytes): its 8 value
+// chunks, then the 16 bytes that end with its scale (record bytes 116..131),
+// so the scale sits at byte 140 of the padded record.
+constexpr int kChunksPerRecord = 9;
+constexpr int kLdsRecord = 16 * kChunksPerRecord;
+constexpr int kDmaBytes = 64 * 16;                        // one 64-lane 16-byte load
+constexpr int kSlotBytes = kIterTokens * kLdsRecord;      // one iteration (9216 bytes)
+constexpr int kGatherLoads = kSlotBytes / kDmaBytes;      // loads per gather (9)
+constexpr int kMaxPages = kIterTokens / 8;                // page ids per iteration (8-token pages)
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -256,74 +261,115 @@ __device__ __forceinline__ void issue_ids(const LogitsParams& p, const Run& c, i
   if (lane < 2 * n_pg) __builtin_amdgcn_global_load_lds(row + lane, LDS_PTR(ids_slot), 4, 0, 0);
 }
 
-// Pages of an iteration's gather, read from its LDS id slot: the page under
-// each 8-token group (wave-uniform) and the page under this lane's token.  An
-// iteration starts at a multiple of 64 tokens and pages hold 8..256 tokens,
-// so token t0 + x lies in page (x >> log2_page) of the iteration.
-struct GatherPages {
-  int64_t group[kDmaPerIter];
-  int64_t lane;
+// Page ids of a gather's 16-byte chunks, read from the iteration's LDS id
+// slot.  Load i of the gather fills LDS chunks 64*i .. 64*i+63 of the slot
+// (lane l: chunk 64*i + l), and chunk q belongs to record q / 9 of the
+// iteration.  An iteration starts at a multiple of 64 tokens and pages hold
+// 8..256 tokens, so record x lies in page (x >> log2_page) of the iteration.
+// Only the low 32 bits of an id are read: a pool that fits in device memory
+// holds fewer than 2^32 pages (the byte offset id * page_bytes is still formed
+// in 64 bits).  Inline assembly with its own LDS wait on purpose: the compiler
+// cannot tell which in-flight LDS-bound loads a plain LDS read could alias and
+// would drain every one of them first, while the ring's ordering already
+// proves these ids have landed.
+struct ChunkPages {
+  uint32_t id[kGatherLoads];
 };
 
-// Inline assembly with its own LDS wait on purpose: the compiler cannot tell
-// which in-flight LDS-bound loads a plain LDS read could alias and would drain
-// every one of them first, while the ring's ordering already proves these ids
-// have landed.
-__device__ __forceinline__ GatherPages read_pages(const int64_t* ids_slot, int lp, int lane) {
+__device__ __forceinline__ ChunkPages read_pages(const int64_t* ids_slot, int lp, int lane) {
+  static_assert(kGatherLoads == 9, "one ds_read_b32 per gather load below");
   const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const int64_t*)ids_slot);
-  uint32_t g[kDmaPerIter];
+  uint32_t g[kGatherLoads];
 #pragma unroll
-  for (int i = 0; i < kDmaPerIter; ++i) g[i] = a + 8u * (uint32_t)((8 * i) >> lp);
-  const uint32_t al = a + 8u * (uint32_t)(lane >> lp);
-  GatherPages r;
+  for (int i = 0; i < kGatherLoads; ++i) {
+    const uint32_t x = (uint32_t)(64 * i + lane) / (uint32_t)kChunksPerRecord;
+    g[i] = a + 8u * (x >> lp);
+  }
+  ChunkPages r;
   asm volatile(
-      "ds_read_b64 %0, %9\n\t"
-      "ds_read_b64 %1, %10\n\t"
-      "ds_read_b64 %2, %11\n\t"
-      "ds_read_b64 %3, %12\n\t"
-      "ds_read_b64 %4, %13\n\t"
-      "ds_read_b64 %5, %14\n\t"
-      "ds_read_b64 %6, %15\n\t"
-      "ds_read_b64 %7, %16\n\t"
-      "ds_read_b64 %8, %17\n\t"
+      "ds_read_b32 %0, %9\n\t"
+      "ds_read_b32 %1, %10\n\t"
+      "ds_read_b32 %2, %11\n\t"
+      "ds_read_b32 %3, %12\n\t"
+      "ds_read_b32 %4, %13\n\t"
+      "ds_read_b32 %5, %14\n\t"
+      "ds_read_b32 %6, %15\n\t"
+      "ds_read_b32 %7, %16\n\t"
+      "ds_read_b32 %8, %17\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.group[0]), "=&v"(r.group[1]), "=&v"(r.group[2]), "=&v"(r.group[3]),
-        "=&v"(r.group[4]), "=&v"(r.group[5]), "=&v"(r.group[6]), "=&v"(r.group[7]),
-        "=&v"(r.lane)
+      : "=&v"(r.id[0]), "=&v"(r.id[1]), "=&v"(r.id[2]), "=&v"(r.id[3]), "=&v"(r.id[4]),
+        "=&v"(r.id[5]), "=&v"(r.id[6]), "=&v"(r.id[7]), "=&v"(r.id[8])
       : "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]), "v"(g[4]), "v"(g[5]), "v"(g[6]), "v"(g[7]),
-        "v"(al)
+        "v"(g[8])
       : "memory");
   return r;
 }
 
-// Issue the gather of one iteration into an LDS slot: 8 loads of 16 bytes per
-// lane for the values (8 tokens per instruction; a page holds at least 8
-// tokens, so an instruction's tokens share one page) and one of 4 bytes per
-// lane for the scales (token = lane).  Exactly kGatherLoads vector memory
-// instructions are issued on every call: lanes at or past `limit` (the
-// context, or 0 for a placeholder gather that only keeps the instruction count
-// fixed) fetch the pool's first record instead and never read their ids, and
-// their results are never stored.
+// Byte offset, inside the iteration's run of 64 records, of the chunk lane
+// `lane` moves in load i: chunk q = 64*i + lane is chunk q % 9 of record q / 9
+// (value chunks at 16*c, the scale chunk at 116).  Depends only on the lane:
+// computed once per wave.
+struct ChunkOffsets {
+  uint32_t off[kGatherLoads];
+};
+
+__device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
+  ChunkOffsets r;
+#pragma unroll
+  for (int i = 0; i < kGatherLoads; ++i) {
+    const int q = 64 * i + lane;
+    const int x = q / kChunksPerRecord;
+    const int c = q - x * kChunksPerRecord;
+    r.off[i] = (uint32_t)(x * kRecordBytes + (c < 8 ? 16 * c : kRecordBytes - 16));
+  }
+  return r;
+}
+
+// Issue the gather of one iteration into an LDS slot: its 64 token records,
+// each as 9 chunks of 16 bytes (8 of values, then the 16 bytes ending with the
+// scale), 9 loads of 16 bytes per lane in all.  A load moves the chunks of
+// about 7 consecutive records, so it reads consecutive cache lines, and the
+// scales come with their records instead of in a separate pass.  Every chunk
+// lies inside its own record.  Exactly kGatherLoads vector memory instructions
+// are issued on every call.
+//  * Pages of 64 tokens or more: the iteration lies in one page, whose base is
+//    wave-uniform; each load adds the lane's fixed chunk offset.  Records past
+//    the context are read from the same page (it is a whole page of the pool)
+//    and never used; a placeholder gather (`limit` 0, only keeping the
+//    instruction count fixed) reads the pool's first 64 records.
+//  * Smaller pages: each chunk takes its record's page id; chunks of records
+//    at or past `limit` fetch from the pool's first KiB instead and never use
+//    their page id.
 __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int limit,
-                                             const int64_t* ids_slot, int lane, uint8_t* slot) {
+                                             const int64_t* ids_slot, int lane,
+                                             const ChunkOffsets& co, uint8_t* slot) {
   const int t0 = it * kIterTokens;
   const int in_page_mask = p.page_size - 1;
-  const int sub = lane >> 3;                 // token within the instruction's 8
-  const int chunk = (lane & 7) ^ sub;        // swizzled 16-byte chunk this lane moves
-  const GatherPages pg = read_pages(ids_slot, p.log2_page, lane);
+  if (p.log2_page >= 6) {
+    const uint32_t a =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const int64_t*)ids_slot);
+    uint32_t id;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(id) : "v"(a) : "memory");
+    id = (uint32_t)uniform((int)id);
+    const int64_t base =
+        t0 < limit ? (int64_t)id * p.page_bytes + (int32_t)((t0 & in_page_mask) * kRecordBytes) : 0;
+    const uint8_t* src = p.kv + base;
 #pragma unroll
-  for (int i = 0; i < kDmaPerIter; ++i) {
-    const int t = t0 + 8 * i + sub;
-    const int64_t off = t < limit ? pg.group[i] * p.page_bytes +
-                                            (int32_t)((t & in_page_mask) * kRecordBytes) + 16 * chunk
-                                      : (int64_t)(16 * chunk);
-    __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * 1024), 16, 0, 0);
+    for (int i = 0; i < kGatherLoads; ++i)
+      __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
+    return;
   }
-  const int t = t0 + lane;
-  const int64_t soff =
-      t < limit ? pg.lane * p.page_bytes + (int32_t)((t & in_page_mask) * kRecordBytes) : 0;
-  __builtin_amdgcn_global_load_lds(p.kv + soff + kHeadDim, LDS_PTR(slot + kSlotValueBytes), 4,
-                                   0, 0);
+  const ChunkPages pg = read_pages(ids_slot, p.log2_page, lane);
+#pragma unroll
+  for (int i = 0; i < kGatherLoads; ++i) {
+    const int x = co.off[i] / kRecordBytes;  // record of the chunk
+    const int t = t0 + x;
+    const int64_t off = t < limit ? (int64_t)pg.id[i] * p.page_bytes +
+                                        (int32_t)((t & in_page_mask) * kRecordBytes +
+                                                  (co.off[i] - x * kRecordBytes))
+                                  : (int64_t)(16 * lane);
+    __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
+  }
 }
 
 // Wait until at most n vector memory instructions are outstanding (n one of
@@ -410,45 +456,46 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
   }
 }
 
-// The iteration's operands from its LDS slot: each lane's two 16-byte halves
-// of its token's 32-byte B operand per tile (chunk c of local token t sits at
-// t*128 + 16*(c ^ (t & 7))) and the scales of those 4 tokens.  Inline
-// assembly with its own LDS wait on purpose: the compiler cannot tell which
-// in-flight LDS-bound loads a plain LDS read could alias and would drain every
-// one of them first (the whole ring), while the explicit vector-memory wait
-// before this read already proves this slot has landed.
+// The iteration's operands from its LDS slot (record x at x * 144, scale at
+// byte 140 of it): per tile, this lane's 32-byte B operand (token m of the
+// tile, value bytes 32*kq .. 32*kq+31) and that token's scale.  The 144-byte
+// stride keeps the 16 lanes of one kq on distinct banks.  Inline assembly with
+// its own LDS wait on purpose: the compiler cannot tell which in-flight
+// LDS-bound loads a plain LDS read could alias and would drain every one of
+// them first (the whole ring), while the explicit vector-memory wait before
+// this read already proves this slot has landed.
 struct SlotOperands {
   v8i kb[kTilesPerIter];
   float sc[kTilesPerIter];
 };
 
 __device__ __forceinline__ SlotOperands read_slot(const uint8_t* slot, int lane) {
-  static_assert(kTilesPerIter == 4 && kTile * 128 == 2048, "offsets below assume 4 tiles of 16 tokens");
+  static_assert(kTilesPerIter == 4 && kTile * kLdsRecord == 2304,
+                "offsets below assume 4 tiles of 16 padded records");
   const int m = lane & 15, kq = lane >> 4;
   const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)slot);
-  // tile t's addresses are tile 0's plus t * 2048 (values) or t * 64 (scales)
-  const uint32_t alo = base + (uint32_t)m * 128u + 16u * (uint32_t)((2 * kq) ^ (m & 7));
-  const uint32_t ahi = base + (uint32_t)m * 128u + 16u * (uint32_t)((2 * kq + 1) ^ (m & 7));
-  const uint32_t as = base + (uint32_t)kSlotValueBytes + 4u * (uint32_t)m;
+  // tile t's addresses are tile 0's plus t * 2304
+  const uint32_t av = base + (uint32_t)(m * kLdsRecord + 32 * kq);
+  const uint32_t as = base + (uint32_t)(m * kLdsRecord + kLdsRecord - 4);
   u32x4 lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
   SlotOperands r;
   asm volatile(
       "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %1, %13\n\t"
-      "ds_read_b128 %2, %12 offset:2048\n\t"
-      "ds_read_b128 %3, %13 offset:2048\n\t"
-      "ds_read_b128 %4, %12 offset:4096\n\t"
-      "ds_read_b128 %5, %13 offset:4096\n\t"
-      "ds_read_b128 %6, %12 offset:6144\n\t"
-      "ds_read_b128 %7, %13 offset:6144\n\t"
-      "ds_read_b32 %8, %14\n\t"
-      "ds_read_b32 %9, %14 offset:64\n\t"
-      "ds_read_b32 %10, %14 offset:128\n\t"
-      "ds_read_b32 %11, %14 offset:192\n\t"
+      "ds_read_b128 %1, %12 offset:16\n\t"
+      "ds_read_b128 %2, %12 offset:2304\n\t"
+      "ds_read_b128 %3, %12 offset:2320\n\t"
+      "ds_read_b128 %4, %12 offset:4608\n\t"
+      "ds_read_b128 %5, %12 offset:4624\n\t"
+      "ds_read_b128 %6, %12 offset:6912\n\t"
+      "ds_read_b128 %7, %12 offset:6928\n\t"
+      "ds_read_b32 %8, %13\n\t"
+      "ds_read_b32 %9, %13 offset:2304\n\t"
+      "ds_read_b32 %10, %13 offset:4608\n\t"
+      "ds_read_b32 %11, %13 offset:6912\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(lo0), "=&v"(hi0), "=&v"(lo1), "=&v"(hi1), "=&v"(lo2), "=&v"(hi2), "=&v"(lo3),
         "=&v"(hi3), "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3])
-      : "v"(alo), "v"(ahi), "v"(as)
+      : "v"(av), "v"(as)
       : "memory");
   const u32x4 lo[kTilesPerIter] = {lo0, lo1, lo2, lo3};
   const u32x4 hi[kTilesPerIter] = {hi0, hi1, hi2, hi3};
@@ -503,7 +550,7 @@ __device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int i
 template <int H, int JW, int WAVES, int RING>
 __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][RING][kSlotBytes];
-  __shared__ __attribute__((aligned(16))) int64_t ids[WAVES][2 * RING][kDmaPerIter];
+  __shared__ __attribute__((aligned(16))) int64_t ids[WAVES][2 * RING][kMaxPages];
   const int lane = threadIdx.x & 63;
   const int m = lane & 15;   // token within a tile (B column / A row)
   const int kq = lane >> 4;  // 32-byte quarter of the head dimension
@@ -522,11 +569,24 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   const int n_it = run.n_it;
   uint8_t* my_ring = &ring[wl][0][0];
   int64_t* my_ids = &ids[wl][0][0];
+  // the gather's per-lane chunk offsets: kept in registers when the wave has
+  // registers to spare (4 waves per CU), recomputed at each gather otherwise
+  // (an opaque copy of the lane index keeps the compiler from hoisting them)
+  const ChunkOffsets co_kept = chunk_offsets(lane);
+  auto offsets = [&]() -> ChunkOffsets {
+    if constexpr (WAVES <= 4) {
+      return co_kept;
+    } else {
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      return chunk_offsets(l);
+    }
+  };
 
   // prologue
 #pragma unroll
   for (int s = 0; s < RING; ++s)
-    if (s < n_it) issue_ids(p, run, run.it0 + s, lane, my_ids + s * kDmaPerIter);
+    if (s < n_it) issue_ids(p, run, run.it0 + s, lane, my_ids + s * kMaxPages);
   QRegs<H, JW> qr;
   if constexpr (RING > 1) load_q<H, JW>(p, run.b, j0, m, kq, qr);
   __builtin_amdgcn_s_waitcnt(0);  // ids of the first R iterations (and q)
@@ -534,11 +594,11 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
 #pragma unroll
   for (int s = 0; s < RING; ++s) {
     if (n_ids < n_it) {
-      issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kDmaPerIter);
+      issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kMaxPages);
       ++n_ids;
     }
-    issue_gather(p, run.it0 + s, s < n_it ? run.ctx_eff : 0, my_ids + s * kDmaPerIter, lane,
-                 my_ring + s * kSlotBytes);
+    issue_gather(p, run.it0 + s, s < n_it ? run.ctx_eff : 0, my_ids + s * kMaxPages, lane,
+                 offsets(), my_ring + s * kSlotBytes);
   }
   // with one slot, the first score waits for every load anyway: q behind the
   // first gather keeps its latency off the path to the K stream
@@ -558,11 +618,11 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
       if (k + RING < n_it) {
         // refill(k): ids of iteration k + 2R, then the gather of k + R
         if (n_ids < n_it) {
-          issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kDmaPerIter);
+          issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kMaxPages);
           ++n_ids;
         }
         issue_gather(p, run.it0 + k + RING, run.ctx_eff,
-                     my_ids + ((k + RING) % (2 * RING)) * kDmaPerIter, lane,
+                     my_ids + ((k + RING) % (2 * RING)) * kMaxPages, lane, offsets(),
                      my_ring + s * kSlotBytes);
       }
     }
