@@ -9,8 +9,9 @@ copies of the inputs and outputs are rotated so that consecutive steps never
 find their K pages in the 256 MB last-level cache.
 
 Prints one JSON line.  `value` is context tokens scored per second over the
-whole step, timed over replays of one HIP graph per rotated input set (the
-kernels back to back, as a serving loop would run them); `roofline` describes
+whole step, timed over replays of one HIP graph holding one step per rotated
+input set (the kernels back to back, as in a serving forward pass that
+captures every layer's indexer step in one graph); `roofline` describes
 the logits kernel (HBM-bound at this shape), its duration the mean of the
 events its dispatches record at kernel start and end over the same number of
 eager steps; `cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample.
@@ -233,35 +234,38 @@ def main():
         for h in e:
             hip.destroy(h)
 
-    # Step throughput: each rotated input set's step (logits then top-k) is
-    # captured once as a HIP graph and the graphs are replayed in turn, as a
-    # serving loop would, so the timed region holds the kernels back to back
-    # without per-launch host overhead.
-    graphs = []
+    # Step throughput: W warm-up steps, then exactly K timed steps, each a
+    # sequence of steps over the rotated input sets (logits then top-k each)
+    # captured in one HIP graph, as a serving forward pass captures its
+    # layers' indexer steps in one graph; the timed region holds the kernels
+    # back to back.
     cap = torch.cuda.Stream(dev)
-    with torch.cuda.stream(cap):
-        for s in range(len(sets)):
-            g = torch.cuda.CUDAGraph()
+
+    def capture(n_steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
                 csh = int(torch.cuda.current_stream(dev).cuda_stream)
-                a = list(largs[s]); a[-1] = csh
-                t = list(targs[s]); t[-1] = csh
-                assert lib.paged_mqa_logits(*a) == 0 and lib.topk_per_row(*t) == 0
-            graphs.append(g)
+                for i in range(n_steps):
+                    a = list(largs[i % len(sets)]); a[-1] = csh
+                    t = list(targs[i % len(sets)]); t[-1] = csh
+                    assert lib.paged_mqa_logits(*a) == 0 and lib.topk_per_row(*t) == 0
+        return g
+
+    warm_graph, timed_graph = capture(max(args.warmup, 1)), capture(args.steps)
     torch.cuda.synchronize()
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
+    warm_graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % len(graphs)].replay()
+    timed_graph.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    step_ms = elapsed * 1e3 / args.steps
+    graph_steps = args.steps
+    step_ms = elapsed * 1e3 / graph_steps
 
     scored = wl.scored_tokens()
     flops = 2.0 * wl.heads * wl.head_dim * scored
-    value = scored * args.steps / elapsed
+    value = scored * graph_steps / elapsed
     lg_avg_s = float(np.mean(logits_ms)) * 1e-3
     abytes = algorithmic_bytes(wl)
     achieved = abytes / lg_avg_s / 1e9
@@ -302,7 +306,7 @@ def main():
                    "heads": wl.heads, "head_dim": wl.head_dim, "page_size": wl.page_size,
                    "context_lens": "U[1,8192]" if args.config == 2 else "see workload",
                    "topk": k, "scored_tokens_per_step": scored, "rotated_input_sets": args.sets},
-        "tflops": flops * args.steps / elapsed / 1e12,
+        "tflops": flops * graph_steps / elapsed / 1e12,
         "eager_ms_per_step": eager_elapsed * 1e3 / args.steps,
         "logits_us": {"mean": lg_avg_s * 1e6, "median": float(np.median(logits_ms)) * 1e3},
         "topk_us": {"mean": float(np.mean(topk_ms)) * 1e3, "median": float(np.median(topk_ms)) * 1e3},

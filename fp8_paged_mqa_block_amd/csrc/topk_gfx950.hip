@@ -7,15 +7,16 @@
 // One 1024-thread workgroup per row runs an exact radix select on
 // order-preserving 32-bit keys.  The design keeps every step off long LDS
 // round-trip chains, which dominate at these sizes:
-//  * the row is loaded once into registers (up to 32 keys a thread; longer
+//  * the row is loaded once into registers (up to 16 keys a thread; longer
 //    rows stream through registers chunk by chunk in every pass);
 //  * the first digit starts right below the bits that every key of the row
 //    shares (the common prefix of the row's largest and smallest key), so
 //    scores that sit in one binade still spread over the bins instead of
 //    piling onto one LDS address;
-//  * digits are 11 bits (2048 bins), so a continuous row is usually resolved
-//    in two passes; a pass stops the select as soon as the bin holding the
-//    k-th key is taken whole;
+//  * digits are 11 bits (2048 bins); the passes stop as soon as the bin
+//    holding the k-th key is taken whole, or, for a row streamed from memory
+//    (where a pass costs a full read), holds at most 256 keys: those are then
+//    gathered (in row order) and ranked against each other directly;
 //  * each pass has two barriers: after the histogram, and after the per-wave
 //    bin totals; sums, prefix sums and min/max inside a wave use DPP row
 //    operations and lane reads, not LDS shuffles;
@@ -38,7 +39,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;  // two bins per thread
 constexpr int kSmallKeys = 8;           // keys per thread for rows up to 8192
-constexpr int kLargeKeys = 32;          // keys per thread (or per chunk) beyond
+constexpr int kLargeKeys = 16;          // keys per thread (or per chunk) beyond
+constexpr int kCandCap = 256;           // bins this small are ranked directly
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -62,6 +64,8 @@ struct TopkShared {
   uint32_t part2[kWaves];        // row min
   uint32_t col_a[2][kWaves];     // per-wave counts of the final pass, by chunk parity
   uint32_t col_e[2][kWaves];
+  alignas(16) uint32_t cand_key[kCandCap];  // keys of the threshold bin, in row order
+  int32_t cand_idx[kCandCap];
 };
 
 // Keys of one chunk: thread (wave w, lane l) holds key j of the chunk at row
@@ -186,12 +190,21 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
       whole_bin = true;  // every key of this bin is in the top k
       break;
     }
+    // a row that streams from memory pays a full read per pass: a bin this
+    // small is ranked directly instead (a pass over keys held in registers is
+    // cheaper than the ranking)
+    if (STREAM && cnt <= (uint32_t)kCandCap) break;
   }
+  // the threshold bin is ranked directly unless it is taken whole or every
+  // bit is fixed (its keys are then equal: row order decides)
+  const bool rank_bin = STREAM && !whole_bin && bits_left > 0;
 
   // ---- write the selection ----
-  // keys above the threshold prefix fill slots [0, k - remaining); keys equal
-  // to it take slots k - remaining + rank, rank in row order, while
-  // rank < remaining (all of them when the bin is taken whole)
+  // keys above the threshold prefix fill slots [0, k - remaining).  Keys in
+  // the threshold bin take slots k - remaining + rank while rank < remaining:
+  // rank in row order when the bin is taken whole or its keys are equal;
+  // otherwise the bin's keys are first gathered (in row order) and each one's
+  // rank among them computed below
   const uint32_t first_eq = (uint32_t)(k - remaining);
   uint32_t run_a = 0, run_e = 0;
   for (int c = 0; c < n_chunks; ++c) {
@@ -225,7 +238,12 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
       if (ok && kp > prefix) out[off_a + (uint32_t)lane_rank(ma)] = idx;
       if (ok && kp == prefix) {
         const uint32_t rank = off_e + (uint32_t)lane_rank(me);
-        if (rank < (uint32_t)remaining) out[first_eq + rank] = idx;
+        if (rank_bin) {
+          sh.cand_key[rank] = ch.key[j];
+          sh.cand_idx[rank] = idx;
+        } else if (rank < (uint32_t)remaining) {
+          out[first_eq + rank] = idx;
+        }
       }
       off_a += (uint32_t)__popcll(ma);
       off_e += (uint32_t)__popcll(me);
@@ -233,7 +251,25 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     run_a += ta;
     run_e += te;
   }
-  (void)whole_bin;
+  if (!rank_bin) return;
+  // rank of each gathered key among the bin's run_e (<= kCandCap) keys:
+  // larger keys first, equal keys in row order (their gather order)
+  __syncthreads();
+  const int nc = (int)run_e;
+  if (tid < nc) {
+    const uint32_t mine = sh.cand_key[tid];
+    int rank = 0;
+    // 4 keys per read; the unused tail of the array is never counted
+#pragma unroll 4
+    for (int i = 0; i < nc; i += 4) {
+      const uint4 o = reinterpret_cast<const uint4*>(sh.cand_key)[i >> 2];
+      rank += (i < nc && (o.x > mine || (o.x == mine && i < tid))) ? 1 : 0;
+      rank += (i + 1 < nc && (o.y > mine || (o.y == mine && i + 1 < tid))) ? 1 : 0;
+      rank += (i + 2 < nc && (o.z > mine || (o.z == mine && i + 2 < tid))) ? 1 : 0;
+      rank += (i + 3 < nc && (o.w > mine || (o.w == mine && i + 3 < tid))) ? 1 : 0;
+    }
+    if (rank < remaining) out[first_eq + rank] = sh.cand_idx[tid];
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
