@@ -12,37 +12,35 @@
 // silent.
 //
 // Mapping onto CDNA4:
-//  * the work is the list of (request, 64-token iteration) pairs over every
-//    context.  A persistent grid of waves splits that list evenly: each wave
-//    scans the context lengths on the device (the host never reads them),
-//    takes a contiguous run of iterations and walks it, so no wave is launched
-//    for an empty chunk and a long context is spread over many waves;
+//  * the work is each request's list of 64-token iterations.  Every wave
+//    reads the context lengths and computes the split itself (the host never
+//    reads them): a request is cut into runs of at most P iterations, P the
+//    smallest length for which every run gets a wave unit, and a wave takes
+//    one run.  A run never leaves its request, so the wave loads its q rows
+//    once, and a long context is spread over many waves;
 //  * a wave also owns a group of up to JW of the next_n rows.  Their q (JW*H x
-//    128 e4m3fn) stays in VGPRs as MFMA A operands, loaded once per request the
-//    wave visits, heads on the M dimension, so each lane ends up holding 4
-//    heads of one token and the head reduction is in-lane FMAs plus two
-//    cross-lane adds;
-//  * K values are staged through LDS by the memory pipeline itself
-//    (global_load_lds_dwordx4): each instruction moves 8 whole token records'
-//    128 value bytes, 16 contiguous bytes per lane, so every load touches only
-//    the cache lines it uses, and no VGPR holds data in flight.  Every wave
-//    keeps a ring of 4 iterations (32 KiB) in flight.  A 16-byte chunk c of
-//    local token t lands at t*128 + 16*(c ^ (t & 7)), so the MFMA B-operand
-//    reads (lane: token t, 32 bytes) hit distinct banks.  The fp32 scales go
-//    to VGPRs (one token per lane) and reach the epilogue lanes by shuffle;
-//  * an instruction's 8 tokens always lie in one page (pages hold >= 8
-//    tokens), so its page base is wave-uniform: pages smaller than the 16-token
-//    matrix tile are assembled into one tile (aiter PR #6626 section 1 builds a
-//    tile from several 8-token pages).  Page ids are read one iteration ahead
-//    of the gather, itself 4 iterations ahead of the matrix work;
+//    128 e4m3fn) stays in VGPRs as MFMA A operands, heads on the M dimension,
+//    so each lane ends up holding 4 heads of one token and the head reduction
+//    is in-lane FMAs plus two cross-lane adds;
+//  * K is staged through LDS by the memory pipeline itself
+//    (global_load_lds_dwordx4): an iteration's 64 token records are copied
+//    whole, 16 bytes per lane per instruction, each record as its 8 value
+//    chunks plus the 16 bytes that end with its scale (144 bytes in LDS), so
+//    every instruction reads consecutive cache lines, no VGPR holds data in
+//    flight and the MFMA B operands come back as aligned 16-byte LDS reads;
+//  * pages hold whole records and at least 8 of them, so pages smaller than
+//    the 16-token matrix tile are assembled into one tile (aiter PR #6626
+//    section 1 builds a tile from several 8-token pages); pages of 64 tokens
+//    or more hold a whole iteration, whose gather is then a wave-uniform page
+//    base plus fixed per-lane offsets.  Page ids are read ahead of the gather;
 //  * page byte offsets are int64 (id * page_size * 132) and the output row
 //    base is int64 (row * out_row_stride) with int32 columns, so pools and
 //    outputs beyond 2^31 bytes are addressed correctly (aiter PR #4244 "Fix";
 //    ATOM PR #2533 "Address Triton decode KV rows with int64 ids");
-//  * workgroups are dealt round-robin over the 8 XCDs, so the grid is
-//    re-indexed to give each XCD a contiguous run of waves: neighbouring runs
-//    of iterations (mostly the same requests) share one L2, which keeps their
-//    q and table rows warm.
+//  * workgroups are dealt round-robin over the 8 XCDs; the grid is re-indexed
+//    so that each XCD gets a contiguous run of workgroups, and the wave units
+//    are dealt wave-major over those workgroups so that every CU gets a share
+//    when the runs are fewer than the waves.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
