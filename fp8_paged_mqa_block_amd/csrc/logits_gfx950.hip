@@ -562,11 +562,24 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   const int unit = (int)(wave / (uint32_t)p.n_rgroups);
   const int j0 = (int)(wave % (uint32_t)p.n_rgroups) * JW;
 
+  uint8_t* my_ring = &ring[wl][0][0];
+  int64_t* my_ids = &ids[wl][0][0];
+  // while the context lengths are read: pull a small block table and q into
+  // L2 (one 4-byte load per 128-byte line, into this wave's idle ring slot;
+  // the gathers that fill the slot later are issued after it, and vector
+  // memory loads complete in order)
+  {
+    const int64_t line = ((int64_t)blockIdx.x * WAVES + wl) * 64 + lane;
+    if (line < p.warm_lines) {
+      const uint8_t* src = line < p.warm_table_lines
+                               ? reinterpret_cast<const uint8_t*>(p.tables) + line * 128
+                               : p.q + (line - p.warm_table_lines) * 128;
+      __builtin_amdgcn_global_load_lds(src, LDS_PTR(my_ring), 4, 0, 0);
+    }
+  }
   Run run;
   if (!find_run(p, unit, lane, run)) return;
   const int n_it = run.n_it;
-  uint8_t* my_ring = &ring[wl][0][0];
-  int64_t* my_ids = &ids[wl][0][0];
   // the gather's per-lane chunk offsets: kept in registers when the wave has
   // registers to spare (4 waves per CU), recomputed at each gather otherwise
   // (an opaque copy of the lane index keeps the compiler from hoisting them)
@@ -633,13 +646,18 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
 // memory stalls) with one iteration in flight each: measured on the decode
 // shape, a second slot per wave made waves stall on issuing its gather behind
 // the saturated memory pipeline before scoring the first, which cost more than
-// the prefetch gained.  Larger units need the registers of a whole SIMD and run
-// 4 waves with 4 iterations in flight.
+// the prefetch gained.  Units of 128 q rows fit two waves per SIMD (8 per
+// workgroup, 2 iterations in flight each): on gfx950 a wave's own matrix and
+// vector instructions barely overlap, so a second wave per SIMD is what keeps
+// the matrix core busy (measured faster than 2 rows per wave at 1 wave per
+// SIMD, despite gathering each page once per row group).  Larger units need
+// the registers of a whole SIMD and run 4 waves with 4 iterations in flight.
 template <int H, int JW>
 struct Geometry {
   static constexpr bool kSmall = H * JW <= 64 && JW <= 3;
-  static constexpr int kWaves = kSmall ? 9 : 4;
-  static constexpr int kRingDepth = kSmall ? 1 : 4;
+  static constexpr bool kMid = H * JW == 128;
+  static constexpr int kWaves = kSmall ? 9 : (kMid ? 8 : 4);
+  static constexpr int kRingDepth = kSmall ? 1 : (kMid ? 2 : 4);
 };
 
 template <int H, int JW>
