@@ -674,41 +674,35 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
   return hipGetLastError();
 }
 
+// Rows per wave: at most kMaxRows(H) (the shapes logits_shape picks).
+template <int H>
+constexpr int kMaxRows = H >= 128 ? 1 : (H >= 64 ? 3 : 4);
+
 template <int H>
 hipError_t launch_heads(const LogitsParams& p, int jw, const LaunchTiming& tm,
                         hipStream_t stream) {
-  if constexpr (H <= 64) {
-    switch (jw) {
-      case 1: return launch_one<H, 1>(p, tm, stream);
-      case 2: return launch_one<H, 2>(p, tm, stream);
-      case 3: return launch_one<H, 3>(p, tm, stream);
-      case 4: return launch_one<H, 4>(p, tm, stream);
-    }
-  } else {
-    switch (jw) {
-      case 1: return launch_one<H, 1>(p, tm, stream);
-      case 2: return launch_one<H, 2>(p, tm, stream);
-    }
+  switch (jw) {
+    case 1: return launch_one<H, 1>(p, tm, stream);
+    case 2: if constexpr (kMaxRows<H> >= 2) return launch_one<H, 2>(p, tm, stream); break;
+    case 3: if constexpr (kMaxRows<H> >= 3) return launch_one<H, 3>(p, tm, stream); break;
+    case 4: if constexpr (kMaxRows<H> >= 4) return launch_one<H, 4>(p, tm, stream); break;
   }
   return hipErrorInvalidValue;
 }
 
 template <int H>
 int waves_per_cu(int jw) {
-  switch (jw) {
-    case 1: return Geometry<H, 1>::kWaves;
-    case 2: return Geometry<H, 2>::kWaves;
-    case 3: return Geometry<H, 3>::kWaves;
-    default: return Geometry<H, 4>::kWaves;
-  }
+  return jw <= 1 ? Geometry<H, 1>::kWaves
+                 : jw == 2 ? Geometry<H, 2>::kWaves
+                           : jw == 3 ? Geometry<H, 3>::kWaves : Geometry<H, 4>::kWaves;
 }
 
 }  // namespace
 
 LogitsShape logits_shape(int heads, int next_n) {
   LogitsShape sh;
-  // at most 256 q rows (128 VGPRs of A operands) per wave
-  const int cap = heads >= 128 ? 1 : (heads >= 64 ? 3 : 4);
+  // rows per wave: measured per head count (at most 192 q rows of A operands)
+  const int cap = heads >= 128 ? kMaxRows<128> : (heads >= 64 ? kMaxRows<64> : kMaxRows<32>);
   sh.rows_per_wave = next_n < cap ? next_n : cap;
   sh.iter_tokens = kIterTokens;
   // one workgroup per CU (its K ring fills most of the CU's LDS)
