@@ -20,6 +20,7 @@ __all__ = [
     "library_path",
     "paged_mqa_logits",
     "topk_per_row",
+    "check_inputs",
     "EXPORTS",
 ]
 
@@ -29,7 +30,7 @@ _lib: Optional[ctypes.CDLL] = None
 
 # Every symbol include/pmqa.h declares.
 EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "topk_per_row", "topk_per_row_timed",
-           "pmqa_status_string", "pmqa_version")
+           "pmqa_check_inputs", "pmqa_status_string", "pmqa_version")
 
 _STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_NULL", 2: "PMQA_ERR_SHAPE", 3: "PMQA_ERR_UNSUPPORTED",
            4: "PMQA_ERR_ALIGNMENT", 5: "PMQA_ERR_HIP"}
@@ -64,6 +65,8 @@ def load_library() -> ctypes.CDLL:
     lib.topk_per_row.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp]
     lib.topk_per_row_timed.restype = ctypes.c_int
     lib.topk_per_row_timed.argtypes = lib.topk_per_row.argtypes + [vp, vp]
+    lib.pmqa_check_inputs.restype = ctypes.c_int
+    lib.pmqa_check_inputs.argtypes = [vp, vp, c_i32, c_i32, c_i64, c_i64, c_i64, vp, vp]
     lib.pmqa_status_string.restype = ctypes.c_char_p
     lib.pmqa_status_string.argtypes = [ctypes.c_int]
     lib.pmqa_version.restype = ctypes.c_int32
@@ -159,3 +162,28 @@ def topk_per_row(logits: torch.Tensor, context_lens: torch.Tensor, k: int, out_i
                           int(B), int(next_n), int(logits.shape[1]), _stream_handle(out_idx, stream))
     _check("topk_per_row", st)
     return out_idx
+
+
+def check_inputs(context_lens: torch.Tensor, block_tables: torch.Tensor, page_size: int,
+                 out_row_stride: int, num_pages: int, stream=None):
+    """Debug check of the device-resident preconditions (synchronises).
+
+    Returns ``(violations, first)``: the number of requests whose context does
+    not fit its table row or output row, or that use a page id outside
+    ``[0, num_pages)``, and the lowest such request index (``B`` when none).
+    """
+    lib = load_library()
+    _need(context_lens.is_cuda and block_tables.is_cuda, "inputs must be device tensors")
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1 and context_lens.is_contiguous(),
+          "context_lens must be contiguous 1-D int32")
+    B = context_lens.shape[0]
+    _need(block_tables.dtype == torch.int64 and block_tables.dim() == 2 and block_tables.shape[0] == B
+          and block_tables.is_contiguous(), "block_tables must be a contiguous [B, W] int64 tensor")
+    result = torch.empty(2, dtype=torch.int32, device=context_lens.device)
+    st = lib.pmqa_check_inputs(context_lens.data_ptr(), block_tables.data_ptr(), int(B), int(page_size),
+                               int(max(block_tables.shape[1], 1)), int(out_row_stride), int(num_pages),
+                               result.data_ptr(), _stream_handle(result, stream))
+    _check("pmqa_check_inputs", st)
+    r = result.cpu()
+    return int(r[0]), int(r[1])
+

@@ -178,4 +178,29 @@ pmqa_status topk_per_row_timed(const float* logits, const int32_t* context_lens,
                    timing(start_event, stop_event));
 }
 
+pmqa_status pmqa_check_inputs(const int32_t* context_lens, const int64_t* block_tables,
+                              int32_t batch, int32_t page_size, int64_t block_table_stride,
+                              int64_t out_row_stride, int64_t num_pages, int32_t* result,
+                              void* stream) {
+  if (batch < 0 || block_table_stride < 1 || out_row_stride < 1 || num_pages < 1)
+    return PMQA_ERR_SHAPE;
+  if (!(page_size == 8 || page_size == 16 || page_size == 32 || page_size == 64 ||
+        page_size == 128 || page_size == 256))
+    return PMQA_ERR_SHAPE;
+  if (!result || (batch > 0 && (!context_lens || !block_tables))) return PMQA_ERR_NULL;
+  if (!aligned(result, 4) || !aligned(context_lens, 4) || !aligned(block_tables, 8))
+    return PMQA_ERR_ALIGNMENT;
+  pmqa::CheckParams p{};
+  p.ctx = context_lens;
+  p.tables = block_tables;
+  p.result = result;
+  p.table_stride = block_table_stride;
+  p.out_stride = out_row_stride;
+  p.num_pages = num_pages;
+  p.page_size = page_size;
+  p.batch = batch;
+  const hipError_t e = pmqa::launch_check(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -60,4 +60,17 @@ struct TopkParams {
 
 hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t stream);
 
+struct CheckParams {
+  const int32_t* ctx;
+  const int64_t* tables;
+  int32_t* result;         // [2]: requests that violate, lowest such request (batch: none)
+  int64_t table_stride;
+  int64_t out_stride;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t batch;
+};
+
+hipError_t launch_check(const CheckParams& p, hipStream_t stream);
+
 }  // namespace pmqa

@@ -154,6 +154,31 @@ PMQA_API pmqa_status topk_per_row_timed(const float* logits, const int32_t* cont
                                         int32_t next_n, int64_t logits_row_stride, void* stream,
                                         void* start_event, void* stop_event);
 
+/*
+ * pmqa_check_inputs - debug check of the preconditions that live in device
+ * memory, which the calls above cannot check without a synchronisation (the
+ * failure classes the pages report: stores silently dropped at large output
+ * strides, aiter PR #4244; wrong pages read through wrapped ids, ATOM PR #2533).
+ * For every request b it checks
+ *     ctx_b <= block_table_stride*page_size  and  ctx_b <= out_row_stride
+ * (negative lengths count as 0, as above), and that every page id the context
+ * uses (entries i < ceil(ctx_b/page_size) of its table row, never past the row)
+ * lies in [0, num_pages).  It reads only context_lens and those table entries
+ * and never dereferences an id.
+ *
+ * context_lens, block_tables  as for paged_mqa_logits.
+ * num_pages     pages in the pool, >= 1.
+ * result        DEVICE int32[2], 4-byte aligned, written by the enqueued work:
+ *               result[0] = number of requests that break a precondition,
+ *               result[1] = the lowest such request index (batch when none).
+ * The call enqueues on `stream` and returns; the caller synchronises and reads
+ * `result`.  Host-checkable argument errors return a status (nothing enqueued).
+ */
+PMQA_API pmqa_status pmqa_check_inputs(const int32_t* context_lens, const int64_t* block_tables,
+                                       int32_t batch, int32_t page_size,
+                                       int64_t block_table_stride, int64_t out_row_stride,
+                                       int64_t num_pages, int32_t* result, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 PMQA_API const char* pmqa_status_string(pmqa_status status);
 

@@ -98,3 +98,20 @@ def test_binding_rejects_wrong_dtypes_before_the_library():
     t = torch.zeros(4, dtype=torch.float32)
     with pytest.raises(ValueError):
         pm.paged_mqa_logits(t, t, t, t, t, 64, 1, t)
+
+
+def check(lib, **kw):
+    a = dict(ctx=P, tab=P, b=4, ps=64, ts=16, ors=1024, np=100, res=P, stream=None)
+    a.update(kw)
+    return lib.pmqa_check_inputs(a["ctx"], a["tab"], a["b"], a["ps"], a["ts"], a["ors"], a["np"],
+                                 a["res"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(res=None), ERR_NULL), (dict(ctx=None), ERR_NULL), (dict(tab=None), ERR_NULL),
+    (dict(b=-1), ERR_SHAPE), (dict(ps=12), ERR_SHAPE), (dict(ts=0), ERR_SHAPE),
+    (dict(ors=0), ERR_SHAPE), (dict(np=0), ERR_SHAPE), (dict(res=P + 2), ERR_ALIGN),
+    (dict(tab=P + 4), ERR_ALIGN),
+])
+def test_check_inputs_host_checks(lib, kw, status):
+    assert check(lib, **kw) == status

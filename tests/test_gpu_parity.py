@@ -307,3 +307,31 @@ def test_graph_replay_matches_eager(gpu_lib, cfg2):
         assert torch.equal(out.view(torch.int32), out_e.view(torch.int32)), f"replay {rep}"
         assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), want), f"replay {rep}"
         run_logits(gpu_lib, wl, d, label="eager between replays")
+
+
+def test_check_inputs_flags_device_preconditions(gpu_lib):
+    """The debug check of device-resident preconditions: clean inputs pass;
+    an out-of-pool id, a negative id and contexts longer than the output row
+    or the table row are reported (lowest request first); entries past a
+    context are never looked at."""
+    wl = synth.make_config(2)
+    tab = wl.block_tables.copy()
+    ctx = wl.context_lens.copy()
+    num_pages = wl.kv_cache.shape[0] if wl.kv_cache.ndim > 1 else wl.kv_cache.size // (wl.page_size * 132)
+    npg = (ctx.astype(np.int64) + wl.page_size - 1) // wl.page_size
+    for b in range(wl.batch):
+        tab[b, npg[b]:] = -5  # unused entries: anything goes
+    d_ctx = torch.from_numpy(ctx).cuda()
+    say("[gpu] pmqa_check_inputs clean")
+    assert gpu_lib.check_inputs(d_ctx, torch.from_numpy(tab).cuda(), wl.page_size,
+                                wl.out_row_stride, num_pages) == (0, wl.batch)
+    bad = tab.copy()
+    bad[7, 0] = num_pages             # past the pool
+    bad[3, npg[3] - 1] = -1           # negative id, last used entry
+    bad_ctx = ctx.copy()
+    bad_ctx[20] = wl.out_row_stride + 1               # longer than the output row
+    bad_ctx[40] = bad.shape[1] * wl.page_size + 64    # longer than the table row
+    say("[gpu] pmqa_check_inputs planted")
+    got = gpu_lib.check_inputs(torch.from_numpy(bad_ctx).cuda(), torch.from_numpy(bad).cuda(),
+                               wl.page_size, wl.out_row_stride, num_pages)
+    assert got == (4, 3), got
