@@ -335,3 +335,31 @@ def test_check_inputs_flags_device_preconditions(gpu_lib):
     got = gpu_lib.check_inputs(torch.from_numpy(bad_ctx).cuda(), torch.from_numpy(bad).cuda(),
                                wl.page_size, wl.out_row_stride, num_pages)
     assert got == (4, 3), got
+
+
+def test_randomized_small_workloads(gpu_lib):
+    """Seeded random shapes across every axis the kernels dispatch on (heads,
+    next_n, page size, batch, context mix incl. zeros, output stride, table
+    width), every row against the oracle, logits and top-k."""
+    rng = np.random.default_rng(2024)
+    for trial in range(12):
+        heads = int(rng.choice([16, 32, 64, 128]))
+        next_n = int(rng.integers(1, 6))
+        ps = int(rng.choice([8, 16, 32, 64, 128, 256]))
+        batch = int(rng.integers(1, 9))
+        ctx = rng.integers(0, 1300, size=batch)
+        ctx[rng.random(batch) < 0.2] = 0
+        wl = synth.build_workload(f"rand{trial}", batch=batch, next_n=next_n, heads=heads,
+                                  head_dim=128, page_size=ps, context_lens=ctx.tolist(),
+                                  table="permuted", topk=int(rng.choice([1, 32, 100])),
+                                  seed=int(rng.integers(1 << 30)),
+                                  table_width=int(-(-max(1, ctx.max()) // ps)) + int(rng.integers(0, 3)))
+        wl.out_row_stride = int(max(1, ctx.max())) + int(rng.integers(0, 50))
+        say(f"[gpu] random trial {trial}: H={heads} next_n={next_n} ps={ps} B={batch} "
+            f"ctx={ctx.tolist()} stride={wl.out_row_stride} k={wl.topk}")
+        d = upload(wl)
+        out = run_logits(gpu_lib, wl, d, label=f"trial={trial}")
+        ref = oracle_rows(wl)
+        check_rows(wl, out, ref)
+        idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+        check_topk(idx, ref, wl.topk)
