@@ -274,15 +274,13 @@ struct ChunkPages {
   uint32_t id[kGatherLoads];
 };
 
-__device__ __forceinline__ ChunkPages read_pages(const int64_t* ids_slot, int lp, int lane) {
+__device__ __forceinline__ ChunkPages read_pages(const int64_t* ids_slot, int lp,
+                                                 const uint32_t (&rec)[kGatherLoads]) {
   static_assert(kGatherLoads == 9, "one ds_read_b32 per gather load below");
   const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const int64_t*)ids_slot);
   uint32_t g[kGatherLoads];
 #pragma unroll
-  for (int i = 0; i < kGatherLoads; ++i) {
-    const uint32_t x = (uint32_t)(64 * i + lane) / (uint32_t)kChunksPerRecord;
-    g[i] = a + 8u * (x >> lp);
-  }
+  for (int i = 0; i < kGatherLoads; ++i) g[i] = a + 8u * (rec[i] >> lp);
   ChunkPages r;
   asm volatile(
       "ds_read_b32 %0, %9\n\t"
@@ -308,7 +306,8 @@ __device__ __forceinline__ ChunkPages read_pages(const int64_t* ids_slot, int lp
 // (value chunks at 16*c, the scale chunk at 116).  Depends only on the lane:
 // computed once per wave.
 struct ChunkOffsets {
-  uint32_t off[kGatherLoads];
+  uint32_t off[kGatherLoads];  // byte offset of the chunk in the iteration's records
+  uint32_t rec[kGatherLoads];  // record (token of the iteration) the chunk lies in
 };
 
 __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
@@ -319,6 +318,7 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
     const int x = q / kChunksPerRecord;
     const int c = q - x * kChunksPerRecord;
     r.off[i] = (uint32_t)(x * kRecordBytes + (c < 8 ? 16 * c : kRecordBytes - 16));
+    r.rec[i] = (uint32_t)x;
   }
   return r;
 }
@@ -357,10 +357,10 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
       __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
     return;
   }
-  const ChunkPages pg = read_pages(ids_slot, p.log2_page, lane);
+  const ChunkPages pg = read_pages(ids_slot, p.log2_page, co.rec);
 #pragma unroll
   for (int i = 0; i < kGatherLoads; ++i) {
-    const int x = co.off[i] / kRecordBytes;  // record of the chunk
+    const int x = (int)co.rec[i];  // record of the chunk
     const int t = t0 + x;
     const int64_t off = t < limit ? (int64_t)pg.id[i] * p.page_bytes +
                                         (int32_t)((t & in_page_mask) * kRecordBytes +
@@ -650,12 +650,16 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
 // workgroup, 2 iterations in flight each): on gfx950 a wave's own matrix and
 // vector instructions barely overlap, so a second wave per SIMD is what keeps
 // the matrix core busy (measured faster than 2 rows per wave at 1 wave per
-// SIMD, despite gathering each page once per row group).  Larger units need
-// the registers of a whole SIMD and run 4 waves with 4 iterations in flight.
+// SIMD, despite gathering each page once per row group).  Units of 192 rows
+// also run two waves per SIMD: they then fill the 256 registers a wave gets
+// there (a few values spill, outside the scoring loop) and were measured about
+// 9% faster than one wave per SIMD with 4 iterations in flight.  Larger units
+// need the registers of a whole SIMD and run 4 waves with 4 iterations in
+// flight.
 template <int H, int JW>
 struct Geometry {
   static constexpr bool kSmall = H * JW <= 64 && JW <= 3;
-  static constexpr bool kMid = H * JW == 128;
+  static constexpr bool kMid = H * JW == 128 || H * JW == 192;
   static constexpr int kWaves = kSmall ? 9 : (kMid ? 8 : 4);
   static constexpr int kRingDepth = kSmall ? 1 : (kMid ? 2 : 4);
 };
