@@ -40,7 +40,9 @@ constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;  // two bins per thread
 constexpr int kSmallKeys = 8;           // keys per thread for rows up to 8192
 constexpr int kLargeKeys = 16;          // keys per thread (or per chunk) beyond
-constexpr int kCandCap = 256;           // bins this small are ranked directly
+constexpr int kCandCap = 256;           // threshold bins this small are ranked directly
+constexpr int kCandCapHeld = 128;       // the same, for rows held in registers
+constexpr int kRankBlock = 32;          // candidates read per ranking step
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -82,23 +84,41 @@ struct Chunk {
       const int64_t i = base + 64 * j;
       key[j] = order_key(row[i < n ? i : n - 1]);
     }
+    set_valid(n, base);
+  }
+
+  // The chunk's raw scores, loaded before the row length is known: the caller
+  // guarantees that the whole span lies inside the row's stride.  finish()
+  // turns them into keys once the length is known.
+  __device__ __forceinline__ void load_span(const float* __restrict__ row, int64_t base) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = __float_as_uint(row[base + 64 * j]);
+  }
+
+  __device__ __forceinline__ void finish(int n, int64_t base) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = order_key(__uint_as_float(key[j]));
+    set_valid(n, base);
+  }
+
+  __device__ __forceinline__ void set_valid(int n, int64_t base) {
+    // key j is inside the row exactly when j < valid
     const int64_t left = (int64_t)n - base;
     valid = left <= 0 ? 0 : (int)min<int64_t>((left + 63) / 64, KPT);
   }
 };
 
+// Selects the row's top k; `ch` holds the row's first chunk (already loaded).
 template <int KPT, bool STREAM>
 __device__ __forceinline__ void select_row(const float* __restrict__ row, int n, int k,
-                           int32_t* __restrict__ out, TopkShared& sh) {
+                                           int32_t* __restrict__ out, TopkShared& sh,
+                                           Chunk<KPT>& ch) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   constexpr int kChunk = kThreads * KPT;
   const int n_chunks = STREAM ? (n + kChunk - 1) / kChunk : 1;
   const int64_t thread_base = (int64_t)wave * 64 * KPT + lane;
-
-  Chunk<KPT> ch;
-  ch.load(row, n, thread_base);
 
   // ---- the row's largest and smallest key ----
   uint32_t kmax = 0u, kmin = ~0u;
@@ -190,14 +210,16 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
       whole_bin = true;  // every key of this bin is in the top k
       break;
     }
-    // a row that streams from memory pays a full read per pass: a bin this
-    // small is ranked directly instead (a pass over keys held in registers is
-    // cheaper than the ranking)
-    if (STREAM && cnt <= (uint32_t)kCandCap) break;
+    // a bin this small is ranked directly instead of refined by another
+    // pass: ranking costs O(cnt^2) LDS reads, so rows held in registers (a
+    // pass costs ~1 us of barriers and LDS round trips) take it only for
+    // small bins, rows that stream from memory (a pass re-reads the row) for
+    // larger ones
+    if (bits_left > 0 && cnt <= (uint32_t)(STREAM ? kCandCap : kCandCapHeld)) break;
   }
   // the threshold bin is ranked directly unless it is taken whole or every
   // bit is fixed (its keys are then equal: row order decides)
-  const bool rank_bin = STREAM && !whole_bin && bits_left > 0;
+  const bool rank_bin = !whole_bin && bits_left > 0;
 
   // ---- write the selection ----
   // keys above the threshold prefix fill slots [0, k - remaining).  Keys in
@@ -259,14 +281,21 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   if (tid < nc) {
     const uint32_t mine = sh.cand_key[tid];
     int rank = 0;
-    // 4 keys per read; the unused tail of the array is never counted
-#pragma unroll 4
-    for (int i = 0; i < nc; i += 4) {
-      const uint4 o = reinterpret_cast<const uint4*>(sh.cand_key)[i >> 2];
-      rank += (i < nc && (o.x > mine || (o.x == mine && i < tid))) ? 1 : 0;
-      rank += (i + 1 < nc && (o.y > mine || (o.y == mine && i + 1 < tid))) ? 1 : 0;
-      rank += (i + 2 < nc && (o.z > mine || (o.z == mine && i + 2 < tid))) ? 1 : 0;
-      rank += (i + 3 < nc && (o.w > mine || (o.w == mine && i + 3 < tid))) ? 1 : 0;
+    // kRankBlock keys per step, all of a step's reads issued together; keys
+    // at or past nc (never written in this call) are not counted
+    for (int i0 = 0; i0 < nc; i0 += kRankBlock) {
+      uint4 o[kRankBlock / 4];
+#pragma unroll
+      for (int u = 0; u < kRankBlock / 4; ++u)
+        o[u] = reinterpret_cast<const uint4*>(sh.cand_key)[(i0 >> 2) + u];
+#pragma unroll
+      for (int u = 0; u < kRankBlock / 4; ++u) {
+        const int i = i0 + 4 * u;
+        rank += (i < nc && (o[u].x > mine || (o[u].x == mine && i < tid))) ? 1 : 0;
+        rank += (i + 1 < nc && (o[u].y > mine || (o[u].y == mine && i + 1 < tid))) ? 1 : 0;
+        rank += (i + 2 < nc && (o[u].z > mine || (o[u].z == mine && i + 2 < tid))) ? 1 : 0;
+        rank += (i + 3 < nc && (o[u].w > mine || (o[u].w == mine && i + 3 < tid))) ? 1 : 0;
+      }
     }
     if (rank < remaining) out[first_eq + rank] = sh.cand_idx[tid];
   }
@@ -278,23 +307,39 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const int r = blockIdx.x;
   const int b = r / p.next_n;
   const int j = r - b * p.next_n;
+  const float* row = p.logits + (int64_t)r * p.row_stride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // When the row's stride spans the first size class, its scores are loaded
+  // before the row length is known, so that the context-length read and this
+  // load overlap instead of running back to back; rows of another class
+  // discard them.
+  const bool early = p.row_stride >= (int64_t)kThreads * kSmallKeys;
+  const int64_t base_small = (int64_t)wave * 64 * kSmallKeys + lane;
+  Chunk<kSmallKeys> first;
+  if (early) first.load_span(row, base_small);
+
   const int ctx = max(p.ctx[b], 0);
   int n = min(max(ctx - p.next_n + j + 1, 0), ctx);
   if ((int64_t)n > p.row_stride) n = (int)p.row_stride;
   const int k = p.k;
   int32_t* out = p.out_idx + (int64_t)r * k;
-  const float* row = p.logits + (int64_t)r * p.row_stride;
 
   if (n <= k) {
     for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
     return;
   }
+  if (n <= kThreads * kSmallKeys) {
+    if (early) first.finish(n, base_small);
+    else first.load(row, n, base_small);
+  }
+  Chunk<kLargeKeys> ch;
+  if (n > kThreads * kSmallKeys) ch.load(row, n, (int64_t)wave * 64 * kLargeKeys + lane);
   if (n <= kThreads * kSmallKeys)
-    select_row<kSmallKeys, false>(row, n, k, out, sh);
+    select_row<kSmallKeys, false>(row, n, k, out, sh, first);
   else if (n <= kThreads * kLargeKeys)
-    select_row<kLargeKeys, false>(row, n, k, out, sh);
+    select_row<kLargeKeys, false>(row, n, k, out, sh, ch);
   else
-    select_row<kLargeKeys, true>(row, n, k, out, sh);
+    select_row<kLargeKeys, true>(row, n, k, out, sh, ch);
 }
 
 }  // namespace

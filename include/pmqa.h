@@ -113,9 +113,13 @@ PMQA_API pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const
  * topk_per_row - indices of the k largest logits of each row (the follow-on
  * top_k_per_row_decode of aiter PR #4244, first paragraph).
  *
- * logits        fp32, row r at element r*logits_row_stride, 4-byte aligned.
- *               Read only on [0, visible(r)) with visible as for
- *               paged_mqa_logits (clamped to logits_row_stride).
+ * logits        fp32 [batch*next_n, logits_row_stride], row r at element
+ *               r*logits_row_stride, 4-byte aligned.  Scores are used only on
+ *               [0, visible(r)) with visible as for paged_mqa_logits (clamped
+ *               to logits_row_stride); the kernel may also load the rest of a
+ *               row's first min(logits_row_stride, 8192) elements (never past
+ *               the row, and their values are never used), so the buffer must
+ *               span every row's stride.
  * context_lens  [batch] int32, as for paged_mqa_logits.
  * k             1 .. 2048.
  * out_idx       [batch*next_n, k] int32, row-major.  Row r receives the
