@@ -108,7 +108,50 @@ struct Chunk {
   }
 };
 
+// The float a key encodes (inverse of order_key; -0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// A first pass over buckets linear in the score, for rows whose scores are all
+// finite: bucket(x) = min(floor((x - lo) * scale), 2047) with lo the row's
+// smallest score and scale = 2048 / (largest - smallest).  Every step is a
+// monotone non-decreasing function of x (rounding included), so a key in a
+// higher bucket is never smaller than one in a lower bucket, and the top k is
+// still selected exactly.  Scores spread like the decode logits put a handful
+// of keys in the threshold bucket, where the common-prefix radix digit (mostly
+// sign and exponent bits) leaves hundreds for a second pass.
+struct Buckets {
+  bool on = false;
+  float lo = 0.f, scale = 0.f;
+
+  __device__ __forceinline__ void setup(uint32_t kmin, uint32_t kmax) {
+    const uint32_t kNegInf = 0x007FFFFFu, kPosInf = 0xFF800000u;  // keys of -inf, +inf
+    if (!(kmin > kNegInf && kmax < kPosInf && kmin < kmax)) return;
+    const float l = key_value(kmin), h = key_value(kmax);
+    const float span = h - l;
+    const float s = (float)kBins / span;
+    if (!(span > 0.f && span <= 3.0e38f && s > 0.f && s <= 3.0e38f)) return;
+    on = true;
+    lo = l;
+    scale = s;
+  }
+
+  __device__ __forceinline__ uint32_t of(uint32_t key) const {
+    const float x = key_value(key);
+    return (uint32_t)__builtin_fminf((x - lo) * scale, (float)(kBins - 1));
+  }
+};
+
 // Selects the row's top k; `ch` holds the row's first chunk (already loaded).
+//
+// Keys are narrowed in passes until the bin holding the k-th largest key is
+// resolved.  On a row held in registers the first pass may bucket by value
+// (Buckets); every later pass takes the next radix digit of the keys that lie
+// in the threshold bucket and match the prefix fixed so far.  A key is then
+// above the threshold when its bucket is higher, or its bucket is the
+// threshold bucket and its fixed bits are higher; it is in the threshold bin
+// when both are equal.
 template <int KPT, bool STREAM>
 __device__ __forceinline__ void select_row(const float* __restrict__ row, int n, int k,
                                            int32_t* __restrict__ out, TopkShared& sh,
@@ -147,11 +190,20 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   int bits_left = kmax == kmin ? 0 : 32 - __builtin_clz(kmax ^ kmin);
   uint32_t mask = high_mask(bits_left);
   uint32_t prefix = kmax & mask;
-  int remaining = k;  // rank of the k-th key among the keys matching prefix
+  int remaining = k;  // rank of the k-th key among the keys in the threshold bin
   bool whole_bin = false;
   int buf = 0;
 
-  // ---- radix passes ----
+  // value buckets of the held keys (all 0 when the row takes radix passes only)
+  Buckets bk;
+  if (!STREAM) bk.setup(kmin, kmax);
+  uint32_t kb[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) kb[j] = bk.on ? bk.of(ch.key[j]) : 0u;
+  uint32_t bstar = 0u;  // the threshold bucket
+  bool bucket_pass = bk.on;
+
+  // ---- passes ----
   while (bits_left > 0) {
     const int width = min(kDigitBits, bits_left);
     const int shift = bits_left - width;
@@ -162,7 +214,11 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const uint32_t key = ch.key[j];
-        if (j < ch.valid && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & dmask], 1u);
+        if (bucket_pass) {
+          if (j < ch.valid) atomicAdd(&h[kb[j]], 1u);
+        } else if (j < ch.valid && kb[j] == bstar && (key & mask) == prefix) {
+          atomicAdd(&h[(key >> shift) & dmask], 1u);
+        }
       }
     }
     __syncthreads();
@@ -202,9 +258,14 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
       digit = bin_hi - 1u; above = a + h1; cnt = h0;
     }
     remaining -= (int)above;
-    prefix |= digit << shift;
-    mask |= dmask << shift;
-    bits_left = shift;
+    if (bucket_pass) {
+      bstar = digit;
+      bucket_pass = false;
+    } else {
+      prefix |= digit << shift;
+      mask |= dmask << shift;
+      bits_left = shift;
+    }
     buf ^= 1;
     if (cnt == (uint32_t)remaining) {
       whole_bin = true;  // every key of this bin is in the top k
@@ -222,8 +283,8 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   const bool rank_bin = !whole_bin && bits_left > 0;
 
   // ---- write the selection ----
-  // keys above the threshold prefix fill slots [0, k - remaining).  Keys in
-  // the threshold bin take slots k - remaining + rank while rank < remaining:
+  // keys above the threshold fill slots [0, k - remaining).  Keys in the
+  // threshold bin take slots k - remaining + rank while rank < remaining:
   // rank in row order when the bin is taken whole or its keys are equal;
   // otherwise the bin's keys are first gathered (in row order) and each one's
   // rank among them computed below
@@ -231,13 +292,16 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   uint32_t run_a = 0, run_e = 0;
   for (int c = 0; c < n_chunks; ++c) {
     if (STREAM) ch.load(row, n, (int64_t)c * kChunk + thread_base);
+    bool is_a[KPT], is_e[KPT];
     uint32_t ca = 0, ce = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const uint32_t kp = ch.key[j] & mask;
       const bool ok = j < ch.valid;
-      ca += (uint32_t)__popcll(__ballot(ok && kp > prefix));
-      ce += (uint32_t)__popcll(__ballot(ok && kp == prefix));
+      is_a[j] = ok && (kb[j] > bstar || (kb[j] == bstar && kp > prefix));
+      is_e[j] = ok && kb[j] == bstar && kp == prefix;
+      ca += (uint32_t)__popcll(__ballot(is_a[j]));
+      ce += (uint32_t)__popcll(__ballot(is_e[j]));
     }
     if (lane == 0) {
       sh.col_a[c & 1][wave] = ca;
@@ -252,13 +316,11 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     const int64_t base = (int64_t)c * kChunk + thread_base;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const uint32_t kp = ch.key[j] & mask;
-      const bool ok = j < ch.valid;
-      const uint64_t ma = __ballot(ok && kp > prefix);
-      const uint64_t me = __ballot(ok && kp == prefix);
+      const uint64_t ma = __ballot(is_a[j]);
+      const uint64_t me = __ballot(is_e[j]);
       const int32_t idx = (int32_t)(base + 64 * j);
-      if (ok && kp > prefix) out[off_a + (uint32_t)lane_rank(ma)] = idx;
-      if (ok && kp == prefix) {
+      if (is_a[j]) out[off_a + (uint32_t)lane_rank(ma)] = idx;
+      if (is_e[j]) {
         const uint32_t rank = off_e + (uint32_t)lane_rank(me);
         if (rank_bin) {
           sh.cand_key[rank] = ch.key[j];

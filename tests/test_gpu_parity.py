@@ -229,7 +229,8 @@ def test_topk_synthetic_rows(gpu_lib, ties):
 def test_topk_special_rows(gpu_lib):
     """Rows the score distribution never produces but the op accepts: one value
     repeated (every key ties), both zeros (equal scores), infinities, subnormals
-    and both signs, at lengths on each side of the register-resident limits."""
+    and both signs, extremes whose difference overflows, a heavy tail, values a
+    few ulps apart, at lengths on each side of the register-resident limits."""
     rng = np.random.default_rng(11)
     rows = []
     for n in (3000, 9000, 40000):
@@ -246,6 +247,15 @@ def test_topk_special_rows(gpu_lib):
         rows.append(mix)
         two = np.where(rng.random(n) < 0.7, np.float32(-2.0), np.float32(3.0)).astype(np.float32)
         rows.append(two)
+        # finite, but the span between the extremes overflows float32
+        rows.append(np.clip(rng.standard_normal(n) * 2e38, -3.4e38, 3.4e38).astype(np.float32))
+        # a heavy tail: most scores share the lowest value bucket
+        rows.append(np.exp(rng.standard_normal(n) * 6.0).astype(np.float32))
+        # eight distinct values one ulp apart
+        rows.append((np.float32(1.0) + rng.integers(0, 8, n).astype(np.float32)
+                     * np.float32(2.0 ** -23)).astype(np.float32))
+        # subnormals only (the bucket scale would overflow)
+        rows.append((rng.integers(-20, 21, n).astype(np.float32) * np.float32(1e-45)).astype(np.float32))
     lens = [len(r) for r in rows]
     width = max(lens)
     dense = np.full((len(rows), width), -np.inf, dtype=np.float32)
