@@ -12,7 +12,10 @@ What it computes (the plain definition, written out):
   tokens a row may see, ``-inf`` for the masked tail of the context, and
   nothing at all past the context (those output columns are left untouched);
 * the top-k token indices per row, ties broken by ascending index, padded
-  with -1 when a row sees fewer than k tokens.
+  with -1 when a row sees fewer than k tokens;
+* the K-cache records the logits read, produced from new K rows (per-token
+  scale amax/448, e4m3fn codes by round-to-nearest-even, records written at
+  int64 slots): ``oracle.k_cache``.
 
 Sources: the op and its tensors are those of ``deepgemm_fp8_paged_mqa_logits``
 (aiter PR #4244 "fix silent tail-row drop in deepgemm_fp8_paged_mqa_logits at
@@ -38,4 +41,11 @@ from .paged_mqa import (  # noqa: F401
     paged_mqa_logits,
     topk_per_row,
     NEG_INF_BITS,
+)
+from .k_cache import (  # noqa: F401,E402
+    e4m3fn_encode,
+    bf16_to_float32,
+    quantize_tokens,
+    record_offset,
+    write_k_cache,
 )
