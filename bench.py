@@ -14,7 +14,9 @@ input set (the kernels back to back, as in a serving forward pass that
 captures every layer's indexer step in one graph); `roofline` describes
 the logits kernel (HBM-bound at this shape), its duration the mean of the
 events its dispatches record at kernel start and end over the same number of
-eager steps; `cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample.
+eager steps; `cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample;
+`k_cache_producer` times the K-cache producer (quantize_k_cache) that writes new
+K rows into the cache, at a decode step's rows and at prefill-sized chunks.
 """
 import argparse
 import hashlib
@@ -105,6 +107,44 @@ def read_traffic(digest):
 def pm_rows_per_wave(wl):
     cap = 1 if wl.heads >= 128 else (3 if wl.heads >= 64 else 4)
     return min(wl.next_n, cap)
+
+
+def measure_k_cache(lib, wl, hip, dev, sh, sizes=(16384, 131072), reps=50):
+    """The K-cache producer on new bf16 K rows written at permuted slots of a
+    pool the size of the workload's: one decode step's rows (batch*next_n), a
+    prefill chunk of 16384 batched tokens, and 131072 tokens (where the kernel
+    leaves its latency floor for the bandwidth regime).  Algorithmic bytes per
+    token: 2*D read + 8 of slot + D+4 written."""
+    import numpy as np
+    import torch
+
+    rng = np.random.default_rng(11)
+    num_slots = wl.num_pages * wl.page_size
+    pool = torch.zeros(num_slots * (wl.head_dim + 4), dtype=torch.uint8, device=dev)
+    gen = torch.Generator().manual_seed(11)
+    out = {}
+    for n in (wl.rows,) + tuple(sizes):
+        k = torch.randn((n, wl.head_dim), generator=gen).to(torch.bfloat16).to(dev)
+        slots = torch.from_numpy(rng.choice(num_slots, n, replace=False).astype(np.int64)).to(dev)
+        args = (k.data_ptr(), 1, slots.data_ptr(), n, wl.head_dim, pool.data_ptr(), num_slots, sh)
+        for _ in range(5):
+            assert lib.quantize_k_cache(*args) == 0
+        ev = [(hip.create(), hip.create()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            assert lib.quantize_k_cache_timed(*args, a, b) == 0
+        torch.cuda.synchronize()
+        us = np.array([hip.elapsed_ms(a, b) for a, b in ev]) * 1e3
+        for a, b in ev:
+            hip.destroy(a)
+            hip.destroy(b)
+        nbytes = n * (2 * wl.head_dim + 8 + wl.head_dim + 4)
+        gbps = nbytes / (us.mean() * 1e-6) / 1e9
+        out[f"tokens_{n}"] = {"us_mean": float(us.mean()), "us_median": float(np.median(us)),
+                              "algorithmic_bytes": nbytes, "GBps": gbps,
+                              "hbm_frac": gbps / HBM_PEAK_GBPS}
+    del pool
+    return out
 
 
 def cpu_baseline(wl, min_seconds=10.0, max_reps=400):
@@ -312,6 +352,7 @@ def main():
         "topk_us": {"mean": float(np.mean(topk_ms)) * 1e3, "median": float(np.median(topk_ms)) * 1e3},
         "logits_tflops": flops / lg_avg_s / 1e12,
         "roofline": roof,
+        "k_cache_producer": measure_k_cache(lib, wl, hip, dev, sh),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)

@@ -21,6 +21,7 @@ __all__ = [
     "paged_mqa_logits",
     "topk_per_row",
     "check_inputs",
+    "quantize_k_cache",
     "EXPORTS",
 ]
 
@@ -30,7 +31,11 @@ _lib: Optional[ctypes.CDLL] = None
 
 # Every symbol include/pmqa.h declares.
 EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "topk_per_row", "topk_per_row_timed",
-           "pmqa_check_inputs", "pmqa_status_string", "pmqa_version")
+           "pmqa_check_inputs", "quantize_k_cache", "quantize_k_cache_timed",
+           "pmqa_status_string", "pmqa_version")
+
+# pmqa_dtype codes of the K rows quantize_k_cache accepts
+_K_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 _STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_NULL", 2: "PMQA_ERR_SHAPE", 3: "PMQA_ERR_UNSUPPORTED",
            4: "PMQA_ERR_ALIGNMENT", 5: "PMQA_ERR_HIP"}
@@ -67,6 +72,10 @@ def load_library() -> ctypes.CDLL:
     lib.topk_per_row_timed.argtypes = lib.topk_per_row.argtypes + [vp, vp]
     lib.pmqa_check_inputs.restype = ctypes.c_int
     lib.pmqa_check_inputs.argtypes = [vp, vp, c_i32, c_i32, c_i64, c_i64, c_i64, vp, vp]
+    lib.quantize_k_cache.restype = ctypes.c_int
+    lib.quantize_k_cache.argtypes = [vp, c_i32, vp, c_i32, c_i32, vp, c_i64, vp]
+    lib.quantize_k_cache_timed.restype = ctypes.c_int
+    lib.quantize_k_cache_timed.argtypes = lib.quantize_k_cache.argtypes + [vp, vp]
     lib.pmqa_status_string.restype = ctypes.c_char_p
     lib.pmqa_status_string.argtypes = [ctypes.c_int]
     lib.pmqa_version.restype = ctypes.c_int32
@@ -162,6 +171,34 @@ def topk_per_row(logits: torch.Tensor, context_lens: torch.Tensor, k: int, out_i
                           int(B), int(next_n), int(logits.shape[1]), _stream_handle(out_idx, stream))
     _check("topk_per_row", st)
     return out_idx
+
+
+def quantize_k_cache(k: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
+                     stream=None) -> torch.Tensor:
+    """Enqueue the K-cache producer: quantise rows of k into the records of kv_cache
+    at their slots (in place; returns kv_cache).
+
+    k            [num_tokens, 128] float32 or bfloat16, contiguous
+    slot_mapping [num_tokens] int64 cache rows (page * page_size + offset); rows
+                 outside the pool (e.g. -1 for padding) are skipped
+    kv_cache     page pool bytes (uint8 or float8_e4m3fn, any contiguous shape);
+                 its byte size / 132 is the number of cache rows
+    """
+    lib = load_library()
+    _byte_view(kv_cache, "kv_cache")
+    for name, t in (("k", k), ("slot_mapping", slot_mapping), ("kv_cache", kv_cache)):
+        _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(k.dtype in _K_DTYPES, f"k must be float32 or bfloat16, got {k.dtype}")
+    _need(k.dim() == 2 and k.is_contiguous(), "k must be a contiguous [num_tokens, head_dim] tensor")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1 and slot_mapping.is_contiguous()
+          and slot_mapping.shape[0] == k.shape[0], "slot_mapping must be contiguous int64 [num_tokens]")
+    _need(kv_cache.is_contiguous(), "kv_cache must be contiguous")
+    num_slots = kv_cache.numel() // (int(k.shape[1]) + 4)
+    st = lib.quantize_k_cache(k.data_ptr(), _K_DTYPES[k.dtype], slot_mapping.data_ptr(),
+                              int(k.shape[0]), int(k.shape[1]), kv_cache.data_ptr(), int(num_slots),
+                              _stream_handle(kv_cache, stream))
+    _check("quantize_k_cache", st)
+    return kv_cache
 
 
 def check_inputs(context_lens: torch.Tensor, block_tables: torch.Tensor, page_size: int,

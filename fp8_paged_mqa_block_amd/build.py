@@ -9,7 +9,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = ["pmqa_host.hip", "logits_gfx950.hip", "topk_gfx950.hip", "check_gfx950.hip"]
+SOURCES = ["pmqa_host.hip", "logits_gfx950.hip", "topk_gfx950.hip", "check_gfx950.hip",
+           "kcache_gfx950.hip"]
 LIB = os.path.join(PKG, "libpmqa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

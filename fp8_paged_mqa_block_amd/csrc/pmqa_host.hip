@@ -28,7 +28,7 @@ const char* pmqa_status_string(pmqa_status status) {
     case PMQA_OK: return "ok";
     case PMQA_ERR_NULL: return "null pointer argument";
     case PMQA_ERR_SHAPE: return "size or stride out of range";
-    case PMQA_ERR_UNSUPPORTED: return "unsupported shape (num_heads must be 16/32/64/128, head_dim 128)";
+    case PMQA_ERR_UNSUPPORTED: return "unsupported shape or dtype (num_heads 16/32/64/128, head_dim 128, k fp32 or bf16)";
     case PMQA_ERR_ALIGNMENT: return "pointer not aligned as required";
     case PMQA_ERR_HIP: return "HIP runtime error at launch";
   }
@@ -131,6 +131,28 @@ pmqa_status topk_impl(const float* logits, const int32_t* context_lens, int32_t 
   return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
 }
 
+pmqa_status kcache_impl(const void* k, int32_t k_dtype, const int64_t* slot_mapping,
+                        int32_t num_tokens, int32_t head_dim, void* kv_cache, int64_t num_slots,
+                        void* stream, const pmqa::LaunchTiming& tm) {
+  if (num_tokens < 0 || num_slots < 0) return PMQA_ERR_SHAPE;
+  if (k_dtype != PMQA_DTYPE_F32 && k_dtype != PMQA_DTYPE_BF16) return PMQA_ERR_UNSUPPORTED;
+  if (head_dim != pmqa::kHeadDim) return PMQA_ERR_UNSUPPORTED;
+  if (num_tokens > 0 && (!k || !slot_mapping || (num_slots > 0 && !kv_cache)))
+    return PMQA_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(slot_mapping, 8) || !aligned(kv_cache, 4))
+    return PMQA_ERR_ALIGNMENT;
+  if (num_tokens == 0) return PMQA_OK;
+  pmqa::KCacheParams p{};
+  p.k = k;
+  p.slots = slot_mapping;
+  p.cache = static_cast<uint8_t*>(kv_cache);
+  p.num_slots = num_slots;
+  p.num_tokens = num_tokens;
+  p.bf16 = k_dtype == PMQA_DTYPE_BF16 ? 1 : 0;
+  const hipError_t e = pmqa::launch_kcache(p, tm, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
+}
+
 pmqa::LaunchTiming timing(void* start_event, void* stop_event) {
   pmqa::LaunchTiming tm;
   tm.start = static_cast<hipEvent_t>(start_event);
@@ -176,6 +198,21 @@ pmqa_status topk_per_row_timed(const float* logits, const int32_t* context_lens,
                                void* stop_event) {
   return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, stream,
                    timing(start_event, stop_event));
+}
+
+pmqa_status quantize_k_cache(const void* k, int32_t k_dtype, const int64_t* slot_mapping,
+                             int32_t num_tokens, int32_t head_dim, void* kv_cache,
+                             int64_t num_slots, void* stream) {
+  return kcache_impl(k, k_dtype, slot_mapping, num_tokens, head_dim, kv_cache, num_slots, stream,
+                     pmqa::LaunchTiming{});
+}
+
+pmqa_status quantize_k_cache_timed(const void* k, int32_t k_dtype, const int64_t* slot_mapping,
+                                   int32_t num_tokens, int32_t head_dim, void* kv_cache,
+                                   int64_t num_slots, void* stream, void* start_event,
+                                   void* stop_event) {
+  return kcache_impl(k, k_dtype, slot_mapping, num_tokens, head_dim, kv_cache, num_slots, stream,
+                     timing(start_event, stop_event));
 }
 
 pmqa_status pmqa_check_inputs(const int32_t* context_lens, const int64_t* block_tables,

@@ -73,4 +73,15 @@ struct CheckParams {
 
 hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 
+struct KCacheParams {
+  const void* k;           // [num_tokens, kHeadDim] fp32 or bf16
+  const int64_t* slots;    // [num_tokens] cache rows
+  uint8_t* cache;          // page pool of num_slots records
+  int64_t num_slots;
+  int32_t num_tokens;
+  int32_t bf16;            // 1: k holds bf16, 0: fp32
+};
+
+hipError_t launch_kcache(const KCacheParams& p, const LaunchTiming& tm, hipStream_t stream);
+
 }  // namespace pmqa

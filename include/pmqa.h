@@ -55,7 +55,7 @@ typedef enum {
   PMQA_OK = 0,
   PMQA_ERR_NULL = 1,        /* a required pointer is NULL                        */
   PMQA_ERR_SHAPE = 2,       /* a size or stride is out of range                  */
-  PMQA_ERR_UNSUPPORTED = 3, /* a valid but unimplemented shape (heads, head_dim) */
+  PMQA_ERR_UNSUPPORTED = 3, /* a valid but unimplemented shape or dtype           */
   PMQA_ERR_ALIGNMENT = 4,   /* a pointer lacks the alignment stated below        */
   PMQA_ERR_HIP = 5          /* the HIP runtime reported an error at launch       */
 } pmqa_status;
@@ -182,6 +182,56 @@ PMQA_API pmqa_status pmqa_check_inputs(const int32_t* context_lens, const int64_
                                        int32_t batch, int32_t page_size,
                                        int64_t block_table_stride, int64_t out_row_stride,
                                        int64_t num_pages, int32_t* result, void* stream);
+
+/* Element types of the K rows quantize_k_cache accepts. */
+typedef enum {
+  PMQA_DTYPE_F32 = 0,  /* IEEE binary32                              */
+  PMQA_DTYPE_BF16 = 1  /* bfloat16: the high 16 bits of a binary32   */
+} pmqa_dtype;
+
+/*
+ * quantize_k_cache - the producer of the records paged_mqa_logits reads:
+ * quantises new K rows to e4m3fn and writes them, with their scales, into the
+ * paged cache at caller-given slots.  The pages name this step through its
+ * addressing only (ATOM PR #2533: the cache kernels compute slots in int64);
+ * the quantisation is the per-token one of the cache's K (fp32 scale =
+ * amax/448, e4m3fn codes), and the record layout is the one paged_mqa_logits
+ * documents (aiter PR #4244 reproducer).
+ *
+ * For each token i in [0, num_tokens), with s = slot_mapping[i]:
+ *     scale = max_d |k[i, d]| / 448  (fp32 division; 1 when the quotient is 0)
+ *     code[d] = e4m3fn(clamp(k[i, d] / scale, -448, 448))  (fp32 division, then
+ *               round to nearest, ties to the even code)
+ * and the record of cache row s, at byte s*(head_dim+4) of kv_cache (formed in
+ * 64-bit), receives the head_dim codes followed by scale (little-endian fp32).
+ *
+ * k             [num_tokens, head_dim] row-major, elements of type k_dtype,
+ *               16-byte aligned.
+ * k_dtype       PMQA_DTYPE_F32 or PMQA_DTYPE_BF16 (widened exactly to fp32).
+ * slot_mapping  [num_tokens] int64 cache rows (page*page_size + offset in the
+ *               page), 8-byte aligned.  Tokens whose slot lies outside
+ *               [0, num_slots) are skipped (padding tokens carry -1).  Two
+ *               tokens must not share a slot (which one lands is unspecified).
+ * num_tokens    >= 0 (0 enqueues nothing).
+ * head_dim      128.
+ * kv_cache      the page pool, num_slots records of head_dim+4 bytes,
+ *               4-byte aligned; only the records of the tokens' slots are
+ *               written.
+ * num_slots     records in the pool (num_pages * page_size), >= 0.
+ * stream        hipStream_t to enqueue on.
+ * Scores of non-finite k rows are outside the contract (the record is written
+ * but its contents are unspecified).
+ */
+PMQA_API pmqa_status quantize_k_cache(const void* k, int32_t k_dtype,
+                                      const int64_t* slot_mapping, int32_t num_tokens,
+                                      int32_t head_dim, void* kv_cache, int64_t num_slots,
+                                      void* stream);
+
+/* quantize_k_cache with dispatch-recorded start/stop events, as the other _timed calls. */
+PMQA_API pmqa_status quantize_k_cache_timed(const void* k, int32_t k_dtype,
+                                            const int64_t* slot_mapping, int32_t num_tokens,
+                                            int32_t head_dim, void* kv_cache, int64_t num_slots,
+                                            void* stream, void* start_event, void* stop_event);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 PMQA_API const char* pmqa_status_string(pmqa_status status);

@@ -115,3 +115,27 @@ def check(lib, **kw):
 ])
 def test_check_inputs_host_checks(lib, kw, status):
     assert check(lib, **kw) == status
+
+
+def kcache(lib, **kw):
+    a = dict(k=P, dt=0, sl=P, n=16, d=128, kv=P, ns=1000, stream=None)
+    a.update(kw)
+    return lib.quantize_k_cache(a["k"], a["dt"], a["sl"], a["n"], a["d"], a["kv"], a["ns"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), ERR_NULL), (dict(sl=None), ERR_NULL), (dict(kv=None), ERR_NULL),
+    (dict(n=-1), ERR_SHAPE), (dict(ns=-1), ERR_SHAPE), (dict(dt=2), ERR_UNSUPPORTED),
+    (dict(dt=-1), ERR_UNSUPPORTED), (dict(d=64), ERR_UNSUPPORTED), (dict(k=P + 8), ERR_ALIGN),
+    (dict(sl=P + 4), ERR_ALIGN), (dict(kv=P + 2), ERR_ALIGN),
+    (dict(n=0, k=None, sl=None, kv=None), OK), (dict(dt=1, n=0), OK),
+])
+def test_quantize_k_cache_host_checks(lib, kw, status):
+    assert kcache(lib, **kw) == status
+
+
+def test_quantize_k_cache_binding_rejects_wrong_dtypes():
+    import torch
+    k = torch.zeros(4, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        pm.quantize_k_cache(k, torch.zeros(4, dtype=torch.int64), torch.zeros(1320, dtype=torch.uint8))
