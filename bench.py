@@ -15,8 +15,10 @@ captures every layer's indexer step in one graph); `roofline` describes
 the logits kernel (HBM-bound at this shape), its duration the mean of the
 events its dispatches record at kernel start and end over the same number of
 eager steps; `cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample;
-`k_cache_producer` times the K-cache producer (quantize_k_cache) that writes new
-K rows into the cache, at a decode step's rows and at prefill-sized chunks.
+`token_level_tables` times the logits on the same pools read through token-level
+tables (page_size 1); `k_cache_producer` times the K-cache producer
+(quantize_k_cache) that writes new K rows into the cache, at a decode step's rows
+and at prefill-sized chunks.
 """
 import argparse
 import hashlib
@@ -107,6 +109,45 @@ def read_traffic(digest):
 def pm_rows_per_wave(wl):
     cap = 1 if wl.heads >= 128 else (3 if wl.heads >= 64 else 4)
     return min(wl.next_n, cap)
+
+
+def measure_token_level(lib, wl, sets, hip, sh, reps=100):
+    """The logits launch on the same rotated pools read through token-level
+    tables (page_size 1: entry t is the pool row of token t), as a dense table
+    of cache row ids addresses them.  Algorithmic bytes as for the paged call,
+    with one 8-byte table entry per token."""
+    import copy
+
+    import numpy as np
+    import torch
+
+    ctx = wl.context_lens.astype(np.int64)
+    tok = np.full((wl.batch, max(1, int(ctx.max()))), wl.poison_page * wl.page_size, dtype=np.int64)
+    for b in range(wl.batch):
+        t = np.arange(ctx[b])
+        tok[b, : ctx[b]] = wl.block_tables[b, t // wl.page_size] * wl.page_size + t % wl.page_size
+    tabs = [torch.from_numpy(tok).to(d["kv"].device) for d in sets]
+    largs = [(d["q"].data_ptr(), d["kv"].data_ptr(), d["w"].data_ptr(), d["ctx"].data_ptr(),
+              t.data_ptr(), 1, wl.next_n, d["out"].data_ptr(), wl.out_row_stride, wl.batch,
+              wl.heads, wl.head_dim, tok.shape[1], sh) for d, t in zip(sets, tabs)]
+    for i in range(10):
+        assert lib.paged_mqa_logits(*largs[i % len(largs)]) == 0
+    ev = [(hip.create(), hip.create()) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        assert lib.paged_mqa_logits_timed(*largs[i % len(largs)], a, b) == 0
+    torch.cuda.synchronize()
+    us = np.array([hip.elapsed_ms(a, b) for a, b in ev]) * 1e3
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    w1 = copy.copy(wl)
+    w1.page_size = 1
+    nbytes = algorithmic_bytes(w1)
+    gbps = nbytes / (us.mean() * 1e-6) / 1e9
+    return {"workload": f"{wl.name} through token-level tables (page_size 1)",
+            "logits_us_mean": float(us.mean()), "logits_us_median": float(np.median(us)),
+            "algorithmic_bytes": nbytes, "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS}
 
 
 def measure_k_cache(lib, wl, hip, dev, sh, sizes=(16384, 131072), reps=50):
@@ -352,6 +393,7 @@ def main():
         "topk_us": {"mean": float(np.mean(topk_ms)) * 1e3, "median": float(np.median(topk_ms)) * 1e3},
         "logits_tflops": flops / lg_avg_s / 1e12,
         "roofline": roof,
+        "token_level_tables": measure_token_level(lib, wl, sets, hip, sh),
         "k_cache_producer": measure_k_cache(lib, wl, hip, dev, sh),
     }
     if not args.no_cpu_baseline:

@@ -28,11 +28,14 @@
 //    chunks plus the 16 bytes that end with its scale (144 bytes in LDS), so
 //    every instruction reads consecutive cache lines, no VGPR holds data in
 //    flight and the MFMA B operands come back as aligned 16-byte LDS reads;
-//  * pages hold whole records and at least 8 of them, so pages smaller than
-//    the 16-token matrix tile are assembled into one tile (aiter PR #6626
-//    section 1 builds a tile from several 8-token pages); pages of 64 tokens
-//    or more hold a whole iteration, whose gather is then a wave-uniform page
-//    base plus fixed per-lane offsets.  Page ids are read ahead of the gather;
+//  * pages hold whole records, a power of two from 1 to 256 of them.  Pages
+//    smaller than the 16-token matrix tile are assembled into one tile (aiter
+//    PR #6626 section 1 builds a tile from several 8-token pages): every
+//    16-byte chunk takes its own record's page id, so token-level tables
+//    (1-token pages: the dense row-id tables of ATOM PR #2533) take the same
+//    path.  Pages of 64 tokens or more hold a whole iteration, whose gather is
+//    then a wave-uniform page base plus fixed per-lane offsets.  Page ids are
+//    read ahead of the gather;
 //  * page byte offsets are int64 (id * page_size * 132) and the output row
 //    base is int64 (row * out_row_stride) with int32 columns, so pools and
 //    outputs beyond 2^31 bytes are addressed correctly (aiter PR #4244 "Fix";
@@ -69,7 +72,7 @@ constexpr int kLdsRecord = 16 * kChunksPerRecord;
 constexpr int kDmaBytes = 64 * 16;                        // one 64-lane 16-byte load
 constexpr int kSlotBytes = kIterTokens * kLdsRecord;      // one iteration (9216 bytes)
 constexpr int kGatherLoads = kSlotBytes / kDmaBytes;      // loads per gather (9)
-constexpr int kMaxPages = kIterTokens / 8;                // page ids per iteration (8-token pages)
+constexpr int kMaxPages = kIterTokens;                    // page ids per iteration (1-token pages)
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -246,27 +249,28 @@ __device__ __forceinline__ void load_q(const LogitsParams& p, int b, int j0, int
 }
 
 // Page ids of an iteration, gathered into LDS by one 4-byte-per-lane load:
-// lanes 2i and 2i+1 move the two halves of the iteration's i-th page id.
-// Only ids inside the context are read (at most 8 pages per iteration).
+// lane i moves the low 32 bits of the iteration's i-th page id (at most 64
+// pages per iteration, with 1-token pages).  Only ids inside the context are
+// read.
 __device__ __forceinline__ void issue_ids(const LogitsParams& p, const Run& c, int it, int lane,
-                                          int64_t* ids_slot) {
+                                          uint32_t* ids_slot) {
   const int t0 = it * kIterTokens;
   const int lp = p.log2_page;
   const int p_first = t0 >> lp;
   const int n_pg = ((min(t0 + kIterTokens, c.ctx_eff) - 1) >> lp) - p_first + 1;
   const uint32_t* row =
       reinterpret_cast<const uint32_t*>(p.tables + (int64_t)c.b * p.table_stride + p_first);
-  if (lane < 2 * n_pg) __builtin_amdgcn_global_load_lds(row + lane, LDS_PTR(ids_slot), 4, 0, 0);
+  if (lane < n_pg) __builtin_amdgcn_global_load_lds(row + 2 * lane, LDS_PTR(ids_slot), 4, 0, 0);
 }
 
 // Page ids of a gather's 16-byte chunks, read from the iteration's LDS id
 // slot.  Load i of the gather fills LDS chunks 64*i .. 64*i+63 of the slot
 // (lane l: chunk 64*i + l), and chunk q belongs to record q / 9 of the
 // iteration.  An iteration starts at a multiple of 64 tokens and pages hold
-// 8..256 tokens, so record x lies in page (x >> log2_page) of the iteration.
-// Only the low 32 bits of an id are read: a pool that fits in device memory
-// holds fewer than 2^32 pages (the byte offset id * page_bytes is still formed
-// in 64 bits).  Inline assembly with its own LDS wait on purpose: the compiler
+// 1..256 tokens (powers of two), so record x lies in page (x >> log2_page) of
+// the iteration.  Only the low 32 bits of an id are staged: a pool that fits
+// in device memory holds fewer than 2^32 pages even of one token (the byte
+// offset id * page_bytes is still formed in 64 bits).  Inline assembly with its own LDS wait on purpose: the compiler
 // cannot tell which in-flight LDS-bound loads a plain LDS read could alias and
 // would drain every one of them first, while the ring's ordering already
 // proves these ids have landed.
@@ -274,13 +278,13 @@ struct ChunkPages {
   uint32_t id[kGatherLoads];
 };
 
-__device__ __forceinline__ ChunkPages read_pages(const int64_t* ids_slot, int lp,
+__device__ __forceinline__ ChunkPages read_pages(const uint32_t* ids_slot, int lp,
                                                  const uint32_t (&rec)[kGatherLoads]) {
   static_assert(kGatherLoads == 9, "one ds_read_b32 per gather load below");
-  const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const int64_t*)ids_slot);
+  const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint32_t*)ids_slot);
   uint32_t g[kGatherLoads];
 #pragma unroll
-  for (int i = 0; i < kGatherLoads; ++i) g[i] = a + 8u * (rec[i] >> lp);
+  for (int i = 0; i < kGatherLoads; ++i) g[i] = a + 4u * (rec[i] >> lp);
   ChunkPages r;
   asm volatile(
       "ds_read_b32 %0, %9\n\t"
@@ -339,13 +343,13 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
 //    at or past `limit` fetch from the pool's first KiB instead and never use
 //    their page id.
 __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int limit,
-                                             const int64_t* ids_slot, int lane,
+                                             const uint32_t* ids_slot, int lane,
                                              const ChunkOffsets& co, uint8_t* slot) {
   const int t0 = it * kIterTokens;
   const int in_page_mask = p.page_size - 1;
   if (p.log2_page >= 6) {
     const uint32_t a =
-        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const int64_t*)ids_slot);
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint32_t*)ids_slot);
     uint32_t id;
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(id) : "v"(a) : "memory");
     id = (uint32_t)uniform((int)id);
@@ -548,7 +552,7 @@ __device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int i
 template <int H, int JW, int WAVES, int RING>
 __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][RING][kSlotBytes];
-  __shared__ __attribute__((aligned(16))) int64_t ids[WAVES][2 * RING][kMaxPages];
+  __shared__ __attribute__((aligned(16))) uint32_t ids[WAVES][2 * RING][kMaxPages];
   const int lane = threadIdx.x & 63;
   const int m = lane & 15;   // token within a tile (B column / A row)
   const int kq = lane >> 4;  // 32-byte quarter of the head dimension
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   const int j0 = (int)(wave % (uint32_t)p.n_rgroups) * JW;
 
   uint8_t* my_ring = &ring[wl][0][0];
-  int64_t* my_ids = &ids[wl][0][0];
+  uint32_t* my_ids = &ids[wl][0][0];
   // while the context lengths are read: pull a small block table and q into
   // L2 (one 4-byte load per 128-byte line, into this wave's idle ring slot;
   // the gathers that fill the slot later are issued after it, and vector

@@ -10,6 +10,8 @@
 namespace {
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+// tokens per page: powers of two from 1 (token-level tables) to 256
+bool valid_page_size(int32_t ps) { return is_pow2(ps) && ps <= 256; }
 
 int log2_exact(int64_t x) {
   int l = 0;
@@ -48,9 +50,7 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
                         int64_t block_table_stride, void* stream, const pmqa::LaunchTiming& tm) {
   if (batch < 0 || next_n < 1 || out_row_stride < 1 || block_table_stride < 1)
     return PMQA_ERR_SHAPE;
-  if (!(page_size == 8 || page_size == 16 || page_size == 32 || page_size == 64 ||
-        page_size == 128 || page_size == 256))
-    return PMQA_ERR_SHAPE;
+  if (!valid_page_size(page_size)) return PMQA_ERR_SHAPE;
   if (head_dim != pmqa::kHeadDim) return PMQA_ERR_UNSUPPORTED;
   if (!(num_heads == 16 || num_heads == 32 || num_heads == 64 || num_heads == 128))
     return PMQA_ERR_UNSUPPORTED;
@@ -221,9 +221,7 @@ pmqa_status pmqa_check_inputs(const int32_t* context_lens, const int64_t* block_
                               void* stream) {
   if (batch < 0 || block_table_stride < 1 || out_row_stride < 1 || num_pages < 1)
     return PMQA_ERR_SHAPE;
-  if (!(page_size == 8 || page_size == 16 || page_size == 32 || page_size == 64 ||
-        page_size == 128 || page_size == 256))
-    return PMQA_ERR_SHAPE;
+  if (!valid_page_size(page_size)) return PMQA_ERR_SHAPE;
   if (!result || (batch > 0 && (!context_lens || !block_tables))) return PMQA_ERR_NULL;
   if (!aligned(result, 4) || !aligned(context_lens, 4) || !aligned(block_tables, 8))
     return PMQA_ERR_ALIGNMENT;

@@ -83,9 +83,11 @@ typedef enum {
  *               ones, never past the row's block_table_stride entries, and never
  *               dereferences them).  Precondition not checked on the host (it
  *               lives in device memory): used ids lie in [0, num_pages).
- * page_size     tokens per page: 8, 16, 32, 64, 128 or 256.  Pages smaller than
- *               the 16-token matrix tile are assembled into one tile (aiter
- *               PR #6626 section 1: a tile is built from several 8-token pages).
+ * page_size     tokens per page: a power of two from 1 to 256.  Pages smaller
+ *               than the 16-token matrix tile are assembled into one tile (aiter
+ *               PR #6626 section 1: a tile is built from several 8-token pages);
+ *               page_size 1 reads token-level tables (a dense table of cache
+ *               row ids, ATOM PR #2533).
  * next_n        MTP query positions per request, >= 1.
  * out           fp32 logits; row r starts at element r*out_row_stride (the row
  *               offset is computed in 64-bit: rows whose byte offset passes

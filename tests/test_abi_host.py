@@ -67,7 +67,7 @@ def logits(lib, **kw):
     (dict(q=None), ERR_NULL), (dict(kv=None), ERR_NULL), (dict(w=None), ERR_NULL),
     (dict(ctx=None), ERR_NULL), (dict(tab=None), ERR_NULL), (dict(out=None), ERR_NULL),
     (dict(nn=0), ERR_SHAPE), (dict(b=-1), ERR_SHAPE), (dict(ors=0), ERR_SHAPE),
-    (dict(ts=0), ERR_SHAPE), (dict(ps=4), ERR_SHAPE), (dict(ps=24), ERR_SHAPE),
+    (dict(ts=0), ERR_SHAPE), (dict(ps=0), ERR_SHAPE), (dict(ps=3), ERR_SHAPE), (dict(ps=24), ERR_SHAPE), (dict(ps=-8), ERR_SHAPE),
     (dict(ps=512), ERR_SHAPE), (dict(d=64), ERR_UNSUPPORTED), (dict(h=48), ERR_UNSUPPORTED),
     (dict(h=256), ERR_UNSUPPORTED), (dict(q=P + 8), ERR_ALIGN), (dict(w=P + 4), ERR_ALIGN),
     (dict(kv=P + 2), ERR_ALIGN), (dict(out=P + 2), ERR_ALIGN), (dict(tab=P + 4), ERR_ALIGN),

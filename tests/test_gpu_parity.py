@@ -45,6 +45,11 @@ SMALL = [
          context_lens=[1, 15]),
     dict(batch=7, next_n=2, heads=32, page_size=8,
          context_lens=[0, 1, 2, 16, 17, 255, 257]),
+    # token-level tables (1-token pages) and the other pages below 8 tokens
+    dict(batch=4, next_n=2, heads=64, page_size=1, ctx_range=(1, 400)),
+    dict(batch=5, next_n=1, heads=128, page_size=1, context_lens=[0, 1, 63, 64, 65]),
+    dict(batch=3, next_n=3, heads=32, page_size=2, ctx_range=(0, 300)),
+    dict(batch=4, next_n=1, heads=16, page_size=4, ctx_range=(1, 500)),
 ]
 
 
@@ -188,6 +193,37 @@ def test_config4_small_pages_compact_and_padded(gpu_lib, cfg4):
     check_topk(idx, ref, wl.topk, rows=rows)
     zrows = [r for b in zero for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
     assert bool((idx[zrows] == -1).all())
+
+
+def token_level_table(wl, table=None):
+    """The same cache rows addressed one token per page: entry t of request b is
+    the pool row of its token t (page * page_size + t % page_size); entries past
+    the context point at the poison page's first row."""
+    tab = wl.block_tables if table is None else table
+    ctx = wl.context_lens.astype(np.int64)
+    out = np.full((wl.batch, max(1, int(ctx.max()))), wl.poison_page * wl.page_size, dtype=np.int64)
+    for b in range(wl.batch):
+        t = np.arange(ctx[b])
+        out[b, : ctx[b]] = tab[b, t // wl.page_size] * wl.page_size + t % wl.page_size
+    return out
+
+
+def test_token_level_table_matches_paged(gpu_lib, cfg4):
+    """Reading the 8-token-page workload's pool through a token-level table
+    (page_size 1) gives bit-identical logits: per-token arithmetic does not
+    depend on how the rows are paged.  The pool holds 16.7M rows, so token ids
+    pass 2^31 / 132 and their byte offsets pass 2^31."""
+    wl = cfg4
+    d = upload(wl)
+    out8 = run_logits(gpu_lib, wl, d, label="8-token pages")
+    tok = token_level_table(wl)
+    assert tok.max() >= 2 ** 31 // (wl.head_dim + 4)
+    out1 = new_out(wl.rows, wl.out_row_stride)
+    say(f"[gpu] paged_mqa_logits token-level table {tok.shape}")
+    gpu_lib.paged_mqa_logits(d["q"], d["kv"], d["w"], d["ctx"], torch.from_numpy(tok).cuda(), 1,
+                             wl.next_n, out1)
+    torch.cuda.synchronize()
+    assert torch.equal(out8.view(torch.int32), out1.view(torch.int32))
 
 
 def test_config5_long_context(gpu_lib):

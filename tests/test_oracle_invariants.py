@@ -67,6 +67,30 @@ def test_identity_vs_permuted_table(ps):
     assert sum(len(x) for x in rows_p) > 0
 
 
+@pytest.mark.parametrize("ps", [2, 8, 64])
+def test_token_level_table_reads_the_same_rows(ps):
+    """The pool read through its page table, and read through a token-level
+    table (page_size 1: entry t is the pool row page * ps + t % ps), give the
+    same scores: the paging changes addresses only."""
+    b = small(seed=12, page_size=ps, ctx_range=(1, 150), table="permuted")
+    ctx = b.context_lens.astype(np.int64)
+    tok = np.full((b.batch, int(ctx.max())), b.poison_page * ps, dtype=np.int64)
+    for r in range(b.batch):
+        t = np.arange(ctx[r])
+        tok[r, : ctx[r]] = b.block_tables[r, t // ps] * ps + t % ps
+    rows_p, _ = run(b)
+    rows_t = oracle.paged_mqa_logits(b.q, b.kv_cache, b.weights, b.context_lens, tok, 1, b.next_n)
+    for x, y in zip(rows_p, rows_t):
+        assert np.array_equal(x, y)
+    # a wrong in-page offset (t // ps in place of t % ps) reads other rows
+    bad = tok.copy()
+    for r in range(b.batch):
+        t = np.arange(ctx[r])
+        bad[r, : ctx[r]] = b.block_tables[r, t // ps] * ps + (t // ps) % ps
+    rows_b = oracle.paged_mqa_logits(b.q, b.kv_cache, b.weights, b.context_lens, bad, 1, b.next_n)
+    assert any(not np.array_equal(x, y) for x, y in zip(rows_p, rows_b))
+
+
 def test_compact_vs_wide_stride_and_batch_split():
     wl = small(seed=2, batch=8, ctx_range=(1, 50))
     compact = int(wl.context_lens.max())
