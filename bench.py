@@ -15,6 +15,7 @@ captures every layer's indexer step in one graph); `roofline` describes
 the logits kernel (HBM-bound at this shape), its duration the mean of the
 events its dispatches record at kernel start and end over the same number of
 eager steps; `cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample;
+`device_copy` is a plain 512 MiB device copy (context for the HBM roofline);
 `token_level_tables` times the logits on the same pools read through token-level
 tables (page_size 1); `k_cache_producer` times the K-cache producer
 (quantize_k_cache) that writes new K rows into the cache, at a decode step's rows
@@ -109,6 +110,29 @@ def read_traffic(digest):
 def pm_rows_per_wave(wl):
     cap = 1 if wl.heads >= 128 else (3 if wl.heads >= 64 else 4)
     return min(wl.next_n, cap)
+
+
+def measure_copy(dev, mib=512, reps=20):
+    """Context for the roofline: a plain device-to-device copy of `mib` MiB
+    (torch's copy kernel), bytes read + written per second, mean over reps."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) * 1e-3 / reps
+    del src, dst
+    gbps = 2 * n / sec / 1e9
+    return {"bytes": 2 * n, "GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS}
 
 
 def measure_token_level(lib, wl, sets, hip, sh, reps=100):
@@ -393,6 +417,7 @@ def main():
         "topk_us": {"mean": float(np.mean(topk_ms)) * 1e3, "median": float(np.median(topk_ms)) * 1e3},
         "logits_tflops": flops / lg_avg_s / 1e12,
         "roofline": roof,
+        "device_copy": measure_copy(dev),
         "token_level_tables": measure_token_level(lib, wl, sets, hip, sh),
         "k_cache_producer": measure_k_cache(lib, wl, hip, dev, sh),
     }
