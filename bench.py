@@ -245,6 +245,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload number (2 = decode B=64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=N_SETS)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the step (no copy, token-level or producer measurements): "
+                         "for profiler runs whose per-kernel figures must cover the step alone")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -417,10 +420,11 @@ def main():
         "topk_us": {"mean": float(np.mean(topk_ms)) * 1e3, "median": float(np.median(topk_ms)) * 1e3},
         "logits_tflops": flops / lg_avg_s / 1e12,
         "roofline": roof,
-        "device_copy": measure_copy(dev),
-        "token_level_tables": measure_token_level(lib, wl, sets, hip, sh),
-        "k_cache_producer": measure_k_cache(lib, wl, hip, dev, sh),
     }
+    if not args.no_extras:
+        res["device_copy"] = measure_copy(dev)
+        res["token_level_tables"] = measure_token_level(lib, wl, sets, hip, sh)
+        res["k_cache_producer"] = measure_k_cache(lib, wl, hip, dev, sh)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res, default=lambda o: o.item() if hasattr(o, "item") else str(o)), flush=True)
