@@ -8,7 +8,7 @@ row, rows whose scale underflows or is subnormal, rows whose quotients sit
 exactly halfway between two codes (scale 1 via an element of 448) or one
 float32 ulp either side, negative values that round to zero.  A second test
 writes rows past 2^31 bytes of the pool; a third feeds the produced cache to
-paged_mqa_logits.
+paged_mqa_logits; a fourth replays the producer from a captured HIP graph.
 """
 import numpy as np
 import pytest
@@ -131,3 +131,31 @@ def test_k_cache_feeds_logits(gpu_lib):
     d["kv"] = pool_dev
     out = run_logits(gpu_lib, wl, d, label="produced cache")
     check_rows(wl, out, oracle_rows(wl))
+
+
+def test_k_cache_graph_replay(gpu_lib):
+    """The producer captured in a HIP graph and replayed with new rows copied into
+    the captured input between replays (the way a serving loop drives it): every
+    replay writes what the oracle writes for the rows of that replay."""
+    n, num_slots = 300, 400
+    rng = np.random.default_rng(21)
+    slots = torch.from_numpy(rng.permutation(num_slots)[:n].astype(np.int64)).cuda()
+    k_in = torch.zeros((n, D), dtype=torch.float32, device="cuda")
+    pool = torch.full((num_slots * REC,), POOL_FILL, dtype=torch.uint8, device="cuda")
+    gpu_lib.quantize_k_cache(k_in, slots, pool)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("[gpu] capture quantize_k_cache graph")
+    with torch.cuda.graph(g):
+        gpu_lib.quantize_k_cache(k_in, slots, pool)
+    for rep in range(3):
+        k32 = _rows(30 + rep, n)[-n:]
+        k_in.copy_(torch.from_numpy(k32))
+        pool.fill_(POOL_FILL)
+        torch.cuda.synchronize()
+        say(f"[gpu] producer graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        want = np.full(num_slots * REC, POOL_FILL, dtype=np.uint8)
+        oracle.write_k_cache(want, k32, slots.cpu().numpy(), D)
+        assert np.array_equal(pool.cpu().numpy(), want), f"replay {rep}"
