@@ -562,27 +562,32 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   // units are dealt wave-major over the workgroups, so that when fewer units
   // than waves have work every CU still gets its share
   const uint32_t wave = (uint32_t)wl * nwg + wg;
-  if (wave >= (uint32_t)p.n_slices * (uint32_t)p.n_rgroups) return;
   const int unit = (int)(wave / (uint32_t)p.n_rgroups);
   const int j0 = (int)(wave % (uint32_t)p.n_rgroups) * JW;
 
   uint8_t* my_ring = &ring[wl][0][0];
   uint32_t* my_ids = &ids[wl][0][0];
-  // while the context lengths are read: pull a small block table and q into
-  // L2 (one 4-byte load per 128-byte line, into this wave's idle ring slot;
-  // the gathers that fill the slot later are issued after it, and vector
-  // memory loads complete in order)
+  // while the context lengths are read: pull a small block table into the L2
+  // of every XCD (each XCD has its own L2, and any wave may need any request's
+  // page ids; workgroups are dealt round-robin over the XCDs, so blockIdx >> 3
+  // numbers this XCD's workgroups) and q into L2 once (its first use waits
+  // behind a gather anyway).  One 4-byte load per 128-byte line, into this
+  // wave's idle ring slot: the gathers that fill the slot later are issued
+  // after them, and vector memory loads complete in order.
   {
-    const int64_t line = ((int64_t)blockIdx.x * WAVES + wl) * 64 + lane;
-    if (line < p.warm_lines) {
-      const uint8_t* src = line < p.warm_table_lines
-                               ? reinterpret_cast<const uint8_t*>(p.tables) + line * 128
-                               : p.q + (line - p.warm_table_lines) * 128;
-      __builtin_amdgcn_global_load_lds(src, LDS_PTR(my_ring), 4, 0, 0);
-    }
+    const int64_t tline = ((int64_t)(blockIdx.x >> 3) * WAVES + wl) * 64 + lane;
+    if (tline < p.warm_table_lines)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(p.tables) + tline * 128,
+                                       LDS_PTR(my_ring), 4, 0, 0);
+    const int64_t qline = ((int64_t)blockIdx.x * WAVES + wl) * 64 + lane;
+    if (qline < p.warm_q_lines)
+      __builtin_amdgcn_global_load_lds(p.q + qline * 128, LDS_PTR(my_ring + 256), 4, 0, 0);
   }
   Run run;
-  if (!find_run(p, unit, lane, run)) return;
+  if (wave >= (uint32_t)p.n_slices * (uint32_t)p.n_rgroups || !find_run(p, unit, lane, run)) {
+    __builtin_amdgcn_s_waitcnt(0);  // the warm-up loads write this workgroup's LDS: land them first
+    return;
+  }
   const int n_it = run.n_it;
   // the gather's per-lane chunk offsets: kept in registers when the wave has
   // registers to spare (4 waves per CU), recomputed at each gather otherwise

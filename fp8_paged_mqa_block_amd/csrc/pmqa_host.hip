@@ -99,10 +99,11 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
   // the context lengths are read, so that the page-id and q loads that depend
   // on them hit L2
   const int64_t kWarmMax = int64_t{4} << 20;
+  const int64_t kWarmTableMax = int64_t{1} << 20;  // per XCD L2 (4 MB each): a quarter at most
   const int64_t table_bytes = (int64_t)batch * block_table_stride * 8;
   const int64_t q_bytes = (int64_t)batch * next_n * num_heads * head_dim;
-  p.warm_table_lines = table_bytes <= kWarmMax ? (table_bytes + 127) / 128 : 0;
-  p.warm_lines = p.warm_table_lines + (q_bytes <= kWarmMax ? q_bytes / 128 : 0);
+  p.warm_table_lines = table_bytes <= kWarmTableMax ? (table_bytes + 127) / 128 : 0;
+  p.warm_q_lines = q_bytes <= kWarmMax ? q_bytes / 128 : 0;
   if (!is_pow2(page_size)) return PMQA_ERR_SHAPE;
 
   hipError_t e = pmqa::launch_logits(p, sh, num_heads, tm, static_cast<hipStream_t>(stream));

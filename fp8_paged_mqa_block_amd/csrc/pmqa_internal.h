@@ -28,8 +28,8 @@ struct LogitsParams {
   int32_t max_tokens;      // min(table_stride*page_size, out_stride), clamped to int32
   int32_t n_slices;        // work units of the grid (>= batch); each takes one run
   int32_t n_rgroups;       // waves per run splitting the next_n rows
-  int64_t warm_table_lines;  // 128-byte lines of the block table to pull into L2 (0: none)
-  int64_t warm_lines;        // + lines of q
+  int64_t warm_table_lines;  // 128-byte lines of the block table to pull into every XCD's L2
+  int64_t warm_q_lines;      // 128-byte lines of q to pull into L2 once (0: none)
 };
 
 // Optional events recorded by the kernel dispatch itself at its start and end.
