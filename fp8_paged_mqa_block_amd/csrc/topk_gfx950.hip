@@ -163,18 +163,39 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   const int n_chunks = STREAM ? (n + kChunk - 1) / kChunk : 1;
   const int64_t thread_base = (int64_t)wave * 64 * KPT + lane;
 
-  // ---- the row's largest and smallest key ----
-  uint32_t kmax = 0u, kmin = ~0u;
-  for (int c = 0; c < n_chunks; ++c) {
-    if (STREAM && c > 0) ch.load(row, n, (int64_t)c * kChunk + thread_base);
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if (j < ch.valid) {
-        kmax = max(kmax, ch.key[j]);
-        kmin = min(kmin, ch.key[j]);
+  // Runs body(chunk, c) over the row's chunks in order; `ch` holds chunk 0 on
+  // entry.  A streamed row alternates two register chunks so that the next
+  // chunk's loads are in flight while the current one is processed (a row of
+  // 128K keys is 8 chunks per pass, each load a full memory latency).
+  Chunk<KPT> nx;
+  auto for_chunks = [&](auto&& body) {
+    if constexpr (!STREAM) {
+      body(ch, 0);
+    } else {
+      for (int c = 0; c < n_chunks; c += 2) {
+        if (c + 1 < n_chunks) nx.load(row, n, (int64_t)(c + 1) * kChunk + thread_base);
+        body(ch, c);
+        if (c + 2 < n_chunks) ch.load(row, n, (int64_t)(c + 2) * kChunk + thread_base);
+        if (c + 1 < n_chunks) body(nx, c + 1);
       }
     }
-  }
+  };
+  // a streamed row's later passes start again from chunk 0
+  auto rewind = [&]() {
+    if constexpr (STREAM) ch.load(row, n, thread_base);
+  };
+
+  // ---- the row's largest and smallest key ----
+  uint32_t kmax = 0u, kmin = ~0u;
+  for_chunks([&](const Chunk<KPT>& cc, int) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (j < cc.valid) {
+        kmax = max(kmax, cc.key[j]);
+        kmin = min(kmin, cc.key[j]);
+      }
+    }
+  });
   kmax = wave_max(kmax);
   kmin = wave_min(kmin);
   if (lane == 0) {
@@ -209,18 +230,18 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     const int shift = bits_left - width;
     const uint32_t dmask = (1u << width) - 1u;
     uint32_t* h = sh.hist[buf];
-    for (int c = 0; c < n_chunks; ++c) {
-      if (STREAM) ch.load(row, n, (int64_t)c * kChunk + thread_base);
+    rewind();
+    for_chunks([&](const Chunk<KPT>& cc, int) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const uint32_t key = ch.key[j];
+        const uint32_t key = cc.key[j];
         if (bucket_pass) {
-          if (j < ch.valid) atomicAdd(&h[kb[j]], 1u);
-        } else if (j < ch.valid && kb[j] == bstar && (key & mask) == prefix) {
+          if (j < cc.valid) atomicAdd(&h[kb[j]], 1u);
+        } else if (j < cc.valid && kb[j] == bstar && (key & mask) == prefix) {
           atomicAdd(&h[(key >> shift) & dmask], 1u);
         }
       }
-    }
+    });
     __syncthreads();
     // the other buffer was last read before this barrier: clear it for the
     // next pass
@@ -290,14 +311,14 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   // rank among them computed below
   const uint32_t first_eq = (uint32_t)(k - remaining);
   uint32_t run_a = 0, run_e = 0;
-  for (int c = 0; c < n_chunks; ++c) {
-    if (STREAM) ch.load(row, n, (int64_t)c * kChunk + thread_base);
+  rewind();
+  for_chunks([&](const Chunk<KPT>& cc, int c) {
     bool is_a[KPT], is_e[KPT];
     uint32_t ca = 0, ce = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const uint32_t kp = ch.key[j] & mask;
-      const bool ok = j < ch.valid;
+      const uint32_t kp = cc.key[j] & mask;
+      const bool ok = j < cc.valid;
       is_a[j] = ok && (kb[j] > bstar || (kb[j] == bstar && kp > prefix));
       is_e[j] = ok && kb[j] == bstar && kp == prefix;
       ca += (uint32_t)__popcll(__ballot(is_a[j]));
@@ -323,7 +344,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
       if (is_e[j]) {
         const uint32_t rank = off_e + (uint32_t)lane_rank(me);
         if (rank_bin) {
-          sh.cand_key[rank] = ch.key[j];
+          sh.cand_key[rank] = cc.key[j];
           sh.cand_idx[rank] = idx;
         } else if (rank < (uint32_t)remaining) {
           out[first_eq + rank] = idx;
@@ -334,7 +355,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     }
     run_a += ta;
     run_e += te;
-  }
+  });
   if (!rank_bin) return;
   // rank of each gathered key among the bin's run_e (<= kCandCap) keys:
   // larger keys first, equal keys in row order (their gather order)
