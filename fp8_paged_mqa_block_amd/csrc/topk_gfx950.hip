@@ -4,19 +4,27 @@
 // #4244, first paragraph): for each row r, the indices of the k largest scores
 // among its visible tokens [0, visible(r)), -1 in the slots left over.
 //
-// One 1024-thread workgroup per row runs an exact radix select on
-// order-preserving 32-bit keys.  The design keeps every step off long LDS
-// round-trip chains, which dominate at these sizes:
-//  * the row is loaded once into registers (up to 16 keys a thread; longer
-//    rows stream through registers chunk by chunk in every pass);
-//  * the first digit starts right below the bits that every key of the row
-//    shares (the common prefix of the row's largest and smallest key), so
-//    scores that sit in one binade still spread over the bins instead of
-//    piling onto one LDS address;
-//  * digits are 11 bits (2048 bins); the passes stop as soon as the bin
-//    holding the k-th key is taken whole, or, for a row streamed from memory
-//    (where a pass costs a full read), holds at most 256 keys: those are then
-//    gathered (in row order) and ranked against each other directly;
+// One 1024-thread workgroup per row runs an exact select on order-preserving
+// 32-bit keys.  The design keeps every step off long LDS round-trip chains,
+// which dominate at these sizes:
+//  * the row is loaded once into registers (up to 16 keys a thread; its first
+//    8192 scores are loaded before the row length is read); longer rows stream
+//    through registers chunk by chunk in every pass, the next chunk's loads in
+//    flight while the current one is processed;
+//  * on a row held in registers whose scores are all finite, the first pass
+//    buckets by value, linearly between the row's smallest and largest score
+//    (monotone, so still exact): on bell-shaped scores the bucket holding the
+//    k-th key keeps a few dozen keys, where a radix digit (mostly sign and
+//    exponent bits) keeps hundreds.  Streamed rows keep radix digits: there
+//    one CU handles up to 128K keys per pass and the bucket's arithmetic costs
+//    more than the pass it saves;
+//  * radix passes take 11-bit digits (2048 bins) of the keys in the threshold
+//    bin, starting below the bits every key of the row shares, so scores in
+//    one binade still spread over the bins instead of piling onto one LDS
+//    address;
+//  * the passes stop as soon as the threshold bin is taken whole, or holds at
+//    most 128 keys (256 for a streamed row, where a pass costs a full read):
+//    those are then gathered in row order and ranked against each other;
 //  * each pass has two barriers: after the histogram, and after the per-wave
 //    bin totals; sums, prefix sums and min/max inside a wave use DPP row
 //    operations and lane reads, not LDS shuffles;
