@@ -381,6 +381,17 @@ def test_check_inputs_flags_device_preconditions(gpu_lib):
     got = gpu_lib.check_inputs(torch.from_numpy(bad_ctx).cuda(), torch.from_numpy(bad).cuda(),
                                wl.page_size, wl.out_row_stride, num_pages)
     assert got == (4, 3), got
+    # the same pool through token-level tables (page_size 1): ids are pool rows
+    tok = token_level_table(wl)
+    rows = num_pages * wl.page_size
+    say("[gpu] pmqa_check_inputs token-level clean")
+    assert gpu_lib.check_inputs(d_ctx, torch.from_numpy(tok).cuda(), 1, wl.out_row_stride,
+                                rows) == (0, wl.batch)
+    tok_bad = tok.copy()
+    tok_bad[11, int(ctx[11]) - 1] = rows  # the last used entry past the pool
+    say("[gpu] pmqa_check_inputs token-level planted")
+    assert gpu_lib.check_inputs(d_ctx, torch.from_numpy(tok_bad).cuda(), 1, wl.out_row_stride,
+                                rows) == (1, 11)
 
 
 def test_randomized_small_workloads(gpu_lib):
