@@ -395,6 +395,16 @@ __device__ __forceinline__ float sum_rows(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// max(x, 0) on the bit pattern: positive floats are positive as int32, and
+// negative ones, -0 and -inf are negative, so the integer max gives x or +0
+// for every non-NaN x (a NaN with the sign bit clear passes through, as the
+// definition's max(0, NaN) does).  One v_max_i32: the float max of a matrix-core
+// result costs two, since the compiler first canonicalizes an operand it
+// cannot prove canonical (v_max_f32 x, x).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Score one iteration (64 tokens x the wave's rows) from its slot operands and
 // store it.  FACTORED: every scale of the iteration is >= 0, so
 // relu(s * x) = s * relu(x) and the scale multiplies the head-weighted sum once
@@ -433,7 +443,7 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (FACTORED)
-            sum = __builtin_fmaf(qr.wv[jj][ht][i], __builtin_fmaxf(acc[ht][i], 0.f), sum);
+            sum = __builtin_fmaf(qr.wv[jj][ht][i], relu_bits(acc[ht][i]), sum);
           else
             sum = __builtin_fmaf(qr.wv[jj][ht][i], __builtin_fmaxf(acc[ht][i] * s, 0.f), sum);
         }
