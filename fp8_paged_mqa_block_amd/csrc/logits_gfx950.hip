@@ -307,11 +307,9 @@ __device__ __forceinline__ ChunkPages read_pages(const uint32_t* ids_slot, int l
 
 // Byte offset, inside the iteration's run of 64 records, of the chunk lane
 // `lane` moves in load i: chunk q = 64*i + lane is chunk q % 9 of record q / 9
-// (value chunks at 16*c, the scale chunk at 116).  Depends only on the lane:
-// computed once per wave.
+// (value chunks at 16*c, the scale chunk at 116).  Depends only on the lane.
 struct ChunkOffsets {
   uint32_t off[kGatherLoads];  // byte offset of the chunk in the iteration's records
-  uint32_t rec[kGatherLoads];  // record (token of the iteration) the chunk lies in
 };
 
 __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
@@ -322,9 +320,18 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
     const int x = q / kChunksPerRecord;
     const int c = q - x * kChunksPerRecord;
     r.off[i] = (uint32_t)(x * kRecordBytes + (c < 8 ? 16 * c : kRecordBytes - 16));
-    r.rec[i] = (uint32_t)x;
   }
   return r;
+}
+
+// The record (token of the iteration) each of the lane's chunks lies in, for
+// the small-page gather; computed there from an opaque copy of the lane so
+// the compiler keeps it out of the page-sized path's registers.
+__device__ __forceinline__ void chunk_records(int lane, uint32_t (&rec)[kGatherLoads]) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+#pragma unroll
+  for (int i = 0; i < kGatherLoads; ++i) rec[i] = (uint32_t)((64 * i + l) / kChunksPerRecord);
 }
 
 // Issue the gather of one iteration into an LDS slot: its 64 token records,
@@ -361,10 +368,12 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
       __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
     return;
   }
-  const ChunkPages pg = read_pages(ids_slot, p.log2_page, co.rec);
+  uint32_t rec[kGatherLoads];
+  chunk_records(lane, rec);
+  const ChunkPages pg = read_pages(ids_slot, p.log2_page, rec);
 #pragma unroll
   for (int i = 0; i < kGatherLoads; ++i) {
-    const int x = (int)co.rec[i];  // record of the chunk
+    const int x = (int)rec[i];  // record of the chunk
     const int t = t0 + x;
     const int64_t off = t < limit ? (int64_t)pg.id[i] * p.page_bytes +
                                         (int32_t)((t & in_page_mask) * kRecordBytes +
@@ -600,11 +609,12 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   }
   const int n_it = run.n_it;
   // the gather's per-lane chunk offsets: kept in registers when the wave has
-  // registers to spare (4 waves per CU), recomputed at each gather otherwise
-  // (an opaque copy of the lane index keeps the compiler from hoisting them)
+  // registers to spare (4 waves per CU, or 128 q rows at two waves per SIMD),
+  // recomputed at each gather otherwise (an opaque copy of the lane index keeps
+  // the compiler from hoisting them)
   const ChunkOffsets co_kept = chunk_offsets(lane);
   auto offsets = [&]() -> ChunkOffsets {
-    if constexpr (WAVES <= 4) {
+    if constexpr (WAVES <= 4 || (WAVES == 8 && H * JW == 128)) {
       return co_kept;
     } else {
       int l = lane;
