@@ -324,16 +324,6 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
   return r;
 }
 
-// The record (token of the iteration) each of the lane's chunks lies in, for
-// the small-page gather; computed there from an opaque copy of the lane so
-// the compiler keeps it out of the page-sized path's registers.
-__device__ __forceinline__ void chunk_records(int lane, uint32_t (&rec)[kGatherLoads]) {
-  int l = lane;
-  asm volatile("" : "+v"(l));
-#pragma unroll
-  for (int i = 0; i < kGatherLoads; ++i) rec[i] = (uint32_t)((64 * i + l) / kChunksPerRecord);
-}
-
 // Issue the gather of one iteration into an LDS slot: its 64 token records,
 // each as 9 chunks of 16 bytes (8 of values, then the 16 bytes ending with the
 // scale), 9 loads of 16 bytes per lane in all.  A load moves the chunks of
@@ -368,17 +358,29 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
       __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
     return;
   }
-  uint32_t rec[kGatherLoads];
-  chunk_records(lane, rec);
-  const ChunkPages pg = read_pages(ids_slot, p.log2_page, rec);
+  // Pages here hold at most 32 tokens and the iteration starts at a multiple
+  // of 64, so record x of the iteration is token (x & (page_size-1)) of page
+  // (x >> log2_page); the chunk's record, its place in the record and its
+  // page are all derived here from one division of the chunk index (an opaque
+  // copy of the lane keeps them out of the page-sized path's registers), and
+  // its address is one 32x32+64-bit multiply-add
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  uint32_t rec[kGatherLoads], in_page[kGatherLoads];
 #pragma unroll
   for (int i = 0; i < kGatherLoads; ++i) {
-    const int x = (int)rec[i];  // record of the chunk
-    const int t = t0 + x;
-    const int64_t off = t < limit ? (int64_t)pg.id[i] * p.page_bytes +
-                                        (int32_t)((t & in_page_mask) * kRecordBytes +
-                                                  (co.off[i] - x * kRecordBytes))
-                                  : (int64_t)(16 * lane);
+    const int q = 64 * i + l;
+    const int x = q / kChunksPerRecord;
+    const int c = q - x * kChunksPerRecord;
+    rec[i] = (uint32_t)x;
+    in_page[i] = (uint32_t)((x & in_page_mask) * kRecordBytes + (c < 8 ? 16 * c : kRecordBytes - 16));
+  }
+  const ChunkPages pg = read_pages(ids_slot, p.log2_page, rec);
+  const uint32_t pb = (uint32_t)p.page_bytes;  // <= 32 records
+#pragma unroll
+  for (int i = 0; i < kGatherLoads; ++i) {
+    const int64_t off = t0 + (int)rec[i] < limit ? (int64_t)((uint64_t)pg.id[i] * pb + in_page[i])
+                                                 : (int64_t)(16 * lane);
     __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
   }
 }
