@@ -112,6 +112,18 @@ def pm_rows_per_wave(wl):
     return min(wl.next_n, cap)
 
 
+def logits_kernel_name(wl):
+    """The logits kernel the library launches for this workload (the host's
+    choice of geometry: one wave per 64-token iteration while every row of a
+    request fits one wave and the grid bound is at most two residencies)."""
+    jw = pm_rows_per_wave(wl)
+    max_tokens = min(wl.block_tables.shape[1] * wl.page_size, wl.out_row_stride)
+    max_iters = wl.batch * ((max_tokens + 63) // 64)
+    if wl.heads * wl.next_n <= 64 and jw == wl.next_n and max_iters <= 2 * 16 * 256:
+        return f"logits_flat_kernel<{wl.heads},{jw}>"
+    return f"logits_kernel<{wl.heads},{jw}>"
+
+
 def measure_copy(dev, mib=512, reps=20):
     """Context for the roofline: a plain device-to-device copy of `mib` MiB
     (torch's copy kernel), bytes read + written per second, mean over reps."""
@@ -389,7 +401,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof.update({
         "traffic": traffic,
-        "kernel": f"logits_kernel<{wl.heads},{pm_rows_per_wave(wl)}>",
+        "kernel": logits_kernel_name(wl),
         "algorithmic_bytes_per_launch": abytes,
         "algorithmic_flops_per_launch": flops,
         "hbm_GBps": achieved,

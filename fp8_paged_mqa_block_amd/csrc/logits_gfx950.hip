@@ -12,6 +12,11 @@
 // silent.
 //
 // Mapping onto CDNA4:
+//  * decode shapes (every next_n row of a request within one wave of 64 q
+//    rows, and a grid bound of at most two residencies) take the flat
+//    geometry of logits_flat_kernel: one single-wave workgroup per 64-token
+//    iteration, the whole grid resident at once.  Other shapes take the
+//    persistent logits_kernel below;
 //  * the work is each request's list of 64-token iterations.  Every wave
 //    reads the context lengths and computes the split itself (the host never
 //    reads them): a request is cut into runs of at most P iterations, P the
@@ -107,17 +112,20 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int lo, int hi) {
 
 // The same 16x16x128 product with exact products and fp32 sums: four chained
 // 16x16x32 f16 MFMAs over the operands' four 8-byte slices.  A and B are sliced
-// identically, so every K index meets its partner exactly once.
-__device__ __forceinline__ v4f mfma_exact(v8i a, const v8h (&b)[4]) {
+// identically, so every K index meets its partner exactly once.  Both slices
+// are converted at their use: the empty asm keeps the compiler from hoisting
+// the converted tiles out of the head and token loops, which would take more
+// registers than q and K occupy in e4m3 (this path serves short rows only, so
+// the repeated conversions cost little).
+__device__ __forceinline__ v4f mfma_exact(v8i a, v8i b) {
   v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    // convert the q slice at its use: the empty asm keeps the compiler from
-    // hoisting all converted q tiles out of the token loop, which would double
-    // the registers q occupies
     int lo = a[2 * c], hi = a[2 * c + 1];
-    asm volatile("" : "+v"(lo), "+v"(hi));
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8_to_f16(lo, hi), b[c], acc, 0, 0, 0);
+    int blo = b[2 * c], bhi = b[2 * c + 1];
+    asm volatile("" : "+v"(lo), "+v"(hi), "+v"(blo), "+v"(bhi));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp8x8_to_f16(lo, hi), fp8x8_to_f16(blo, bhi),
+                                                 acc, 0, 0, 0);
   }
   return acc;
 }
@@ -435,17 +443,12 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
 #pragma unroll
   for (int tile = 0; tile < kTilesPerIter; ++tile) {
     const float s = sc[tile];
-    v8h kh[4];
-    if constexpr (EXACT) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) kh[q] = fp8x8_to_f16(kb[tile][2 * q], kb[tile][2 * q + 1]);
-    }
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
       v4f acc[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        if constexpr (EXACT) acc[ht] = mfma_exact(qr.qa[jj][ht], kh);
+        if constexpr (EXACT) acc[ht] = mfma_exact(qr.qa[jj][ht], kb[tile]);
         else acc[ht] = mfma_fp8(qr.qa[jj][ht], kb[tile]);
       }
       float sum = 0.f;
@@ -532,12 +535,12 @@ __device__ __forceinline__ SlotOperands read_slot(const uint8_t* slot, int lane)
   return r;
 }
 
+// Score one iteration from its operands, already read from the slot.
 template <int H, int JW>
-__device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int it, int j0, int lane,
-                                      const QRegs<H, JW>& qr, const uint8_t* slot) {
+__device__ __forceinline__ void score_ops(const LogitsParams& p, const Run& c, int it, int j0,
+                                          int lane, const QRegs<H, JW>& qr, SlotOperands op) {
   // the wave's first row sees the fewest tokens
   const int min_vis = min(max(c.ctx - p.next_n + j0 + 1, 0), c.ctx);
-  SlotOperands op = read_slot(slot, lane);
   const int t0 = it * kIterTokens + (lane & 15);
   bool bad = false;
 #pragma unroll
@@ -554,6 +557,12 @@ __device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int i
     if (factored) score_iteration<H, JW, false, true>(p, c, it, j0, lane, qr, op.kb, op.sc);
     else score_iteration<H, JW, false, false>(p, c, it, j0, lane, qr, op.kb, op.sc);
   }
+}
+
+template <int H, int JW>
+__device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int it, int j0, int lane,
+                                      const QRegs<H, JW>& qr, const uint8_t* slot) {
+  score_ops<H, JW>(p, c, it, j0, lane, qr, read_slot(slot, lane));
 }
 
 // H heads; JW next_n rows per wave; WAVES waves per workgroup (one workgroup
@@ -671,6 +680,117 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
   }
 }
 
+// Flat geometry for small units (all next_n rows of a request within 64 q
+// rows): a work item is one 64-token iteration of one request, and every wave
+// is a workgroup of its own.  The grid is at most one residency of the chip
+// (16 such waves per CU), so no wave is dispatched behind the K stream, where
+// its first loads would queue behind the whole gather traffic.  Workgroup g
+// runs on XCD g % 8 (the dispatcher deals workgroups round-robin over the
+// XCDs); XCD x takes a contiguous eighth of the request-ordered item list, and
+// its waves take contiguous, nearly equal shares of that, the longer shares
+// going to the waves dispatched first.  Consecutive items of a wave are then
+// mostly consecutive iterations of one request, whose q rows stay in
+// registers, and consecutive waves on an XCD read the same q rows and table
+// lines from that XCD's L2.  One K slot per wave, refilled once its item is
+// scored; the page ids of the next item travel with the current gather.  The
+// host takes this geometry only when the possible iterations are at most two
+// residencies, so a share holds one or two items.
+__device__ __forceinline__ void locate_item(const LogitsParams& p, uint32_t e, int lane,
+                                            uint32_t n0, int ctx0, uint32_t incl0,
+                                            uint32_t chunk0, Run& run) {
+  uint32_t before = 0, n = n0, incl = incl0, chunk = chunk0;
+  int ctx = ctx0;
+  for (int c0 = 0;;) {
+    if (before + chunk > e) {
+      const uint64_t past = __ballot(before + incl > e);
+      const int f = uniform(__builtin_ctzll(past));
+      run.b = c0 + f;
+      run.ctx = (int)lane_of((uint32_t)ctx, f);
+      run.ctx_eff = min(run.ctx, p.max_tokens);
+      run.it0 = (int)(e - (before + lane_of(incl, f) - lane_of(n, f)));
+      run.n_it = 1;
+      return;
+    }
+    before += chunk;
+    c0 += 64;
+    if (c0 >= p.batch) return;  // not reached: the caller passes e < total
+    n = (uint32_t)lane_iters(p, c0, lane, ctx);
+    incl = wave_prefix(n, lane, chunk);
+  }
+}
+
+// The item after `cur`: its next iteration, or the first of a later request.
+__device__ __forceinline__ void next_item(const LogitsParams& p, const Run& cur, uint32_t e,
+                                         int lane, uint32_t n0, int ctx0, uint32_t incl0,
+                                         uint32_t chunk0, Run& nxt) {
+  if (cur.it0 + 1 < n_iters(cur.ctx, p.max_tokens)) {
+    nxt = cur;
+    nxt.it0 = cur.it0 + 1;
+  } else {
+    locate_item(p, e, lane, n0, ctx0, incl0, chunk0, nxt);
+  }
+}
+
+template <int H, int JW>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void logits_flat_kernel(LogitsParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t slot[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t ids[2][kMaxPages];
+  const int lane = threadIdx.x;
+  const int m = lane & 15;
+  const int kq = lane >> 4;
+  const uint32_t xcd = blockIdx.x & 7u;
+  const uint32_t k = blockIdx.x >> 3;
+  const uint32_t kx = gridDim.x >> 3;  // waves per XCD
+  // iterations of every request
+  int ctx0;
+  const uint32_t n0 = (uint32_t)lane_iters(p, 0, lane, ctx0);
+  uint32_t chunk0;
+  const uint32_t incl0 = wave_prefix(n0, lane, chunk0);
+  uint32_t total = chunk0;
+  for (int c0 = 64; c0 < p.batch; c0 += 64) {
+    int ctx;
+    total += wave_sum((uint32_t)lane_iters(p, c0, lane, ctx));
+  }
+  // this wave's share: items [e, e + cnt) of the list
+  const uint32_t per = (total + 7u) >> 3;
+  const uint32_t lo = min(xcd * per, total);
+  const uint32_t nx = min(lo + per, total) - lo;
+  const uint32_t a = nx / kx, r = nx % kx;
+  const uint32_t cnt = a + (k < r ? 1u : 0u);
+  if (cnt == 0) return;
+  uint32_t e = lo + k * a + min(k, r);
+
+  // at most two items: the grid covers at least half of the possible ones
+  Run cur, nxt;
+  locate_item(p, e, lane, n0, ctx0, incl0, chunk0, cur);
+  issue_ids(p, cur, cur.it0, lane, ids[0]);
+  __builtin_amdgcn_s_waitcnt(0);  // page ids in LDS
+  issue_gather(p, cur.it0, cur.ctx_eff, ids[0], lane, chunk_offsets(lane), slot);
+  if (cnt > 1) {
+    next_item(p, cur, e + 1, lane, n0, ctx0, incl0, chunk0, nxt);
+    issue_ids(p, nxt, nxt.it0, lane, ids[1]);
+  }
+  QRegs<H, JW> qr;
+  load_q<H, JW>(p, cur.b, 0, m, kq, qr);
+  __builtin_amdgcn_s_waitcnt(0);  // the gather, q and the next item's ids
+  score<H, JW>(p, cur, cur.it0, 0, lane, qr, slot);
+  if (cnt == 1) return;
+  // the slot reads are done (read_slot waits for them): refill it.  The next
+  // item's fields and the lane pass through empty asm so that its addresses
+  // are formed here, not early and spilled: a spill reload between the
+  // gather's loads would wait for every load issued before it.
+  int l2 = lane;
+  nxt.it0 = uniform(nxt.it0);
+  nxt.ctx_eff = uniform(nxt.ctx_eff);
+  nxt.b = uniform(nxt.b);
+  asm volatile("" : "+v"(l2), "+s"(nxt.it0), "+s"(nxt.ctx_eff), "+s"(nxt.b));
+  issue_gather(p, nxt.it0, nxt.ctx_eff, ids[1], l2, chunk_offsets(l2), slot);
+  if (nxt.b != cur.b) load_q<H, JW>(p, nxt.b, 0, m, kq, qr);
+  __builtin_amdgcn_s_waitcnt(0);
+  score<H, JW>(p, nxt, nxt.it0, 0, lane, qr, slot);
+}
+
 // Launch geometry per instantiation.  Wave units of at most 64 q rows (and at
 // most 3 next_n rows, whose partial sums also take registers) run 9 waves per
 // workgroup (2-3 per SIMD, so that one wave's matrix work overlaps another's
@@ -697,6 +817,19 @@ struct Geometry {
 
 template <int H, int JW>
 hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t stream) {
+  if constexpr (H * JW <= 64) {
+    if (p.flat_items > 0) {
+      // at most one residency: 16 single-wave workgroups per CU, 32 CUs per XCD
+      const int64_t per_xcd = (p.flat_items + 7) / 8;
+      const uint32_t n_wg = 8u * (uint32_t)(per_xcd < 16 * 32 ? per_xcd : 16 * 32);
+      auto kern = logits_flat_kernel<H, JW>;
+      if (tm.start || tm.stop)
+        hipExtLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, tm.start, tm.stop, 0, p);
+      else
+        hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   using G = Geometry<H, JW>;
   uint32_t n_wg = ((uint32_t)p.n_slices * (uint32_t)p.n_rgroups + G::kWaves - 1) / G::kWaves;
   n_wg = (n_wg + 7u) & ~7u;
@@ -749,6 +882,9 @@ LogitsShape logits_shape(int heads, int next_n) {
     case 128: per_cu = waves_per_cu<128>(sh.rows_per_wave); break;
   }
   sh.target_waves = 256 * per_cu;
+  // flat geometry: every row of a request in one wave of at most 64 q rows, and
+  // at most two residencies of 16 single-wave workgroups per CU
+  sh.flat_max_items = heads * next_n <= 64 && sh.rows_per_wave == next_n ? 2 * 16 * 256 : 0;
   return sh;
 }
 

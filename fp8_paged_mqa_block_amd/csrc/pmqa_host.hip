@@ -95,6 +95,7 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
   if (n_slices > INT32_MAX / n_rgroups) n_slices = INT32_MAX / n_rgroups;  // still >= batch
   p.n_slices = (int32_t)n_slices;
   p.n_rgroups = (int32_t)n_rgroups;
+  p.flat_items = n_rgroups == 1 && max_iters <= sh.flat_max_items ? max_iters : 0;
   // small block tables and q rows are pulled into L2 at kernel start, while
   // the context lengths are read, so that the page-id and q loads that depend
   // on them hit L2

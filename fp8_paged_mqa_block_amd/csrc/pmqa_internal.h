@@ -30,6 +30,7 @@ struct LogitsParams {
   int32_t n_rgroups;       // waves per run splitting the next_n rows
   int64_t warm_table_lines;  // 128-byte lines of the block table to pull into every XCD's L2
   int64_t warm_q_lines;      // 128-byte lines of q to pull into L2 once (0: none)
+  int64_t flat_items;        // > 0: flat geometry over this many possible iterations
 };
 
 // Optional events recorded by the kernel dispatch itself at its start and end.
@@ -43,6 +44,8 @@ struct LogitsShape {
   int rows_per_wave;  // next_n rows one wave holds (JW)
   int iter_tokens;    // tokens per iteration of a wave
   int target_waves;   // waves of the persistent grid when there is enough work
+  int flat_max_items; // flat geometry when every row of a request fits one wave and
+                      // the possible iterations are at most this many (0: never)
 };
 LogitsShape logits_shape(int heads, int next_n);
 hipError_t launch_logits(const LogitsParams& p, const LogitsShape& sh, int heads,
