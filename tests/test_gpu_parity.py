@@ -394,6 +394,39 @@ def test_check_inputs_flags_device_preconditions(gpu_lib):
                                 rows) == (1, 11)
 
 
+FLAT = [
+    # batch > 64 (the item search walks several 64-request chunks) and more
+    # 64-token iterations than one residency of single-wave workgroups (4096),
+    # so shares of two items occur, some crossing into the next request
+    dict(batch=200, next_n=1, heads=64, page_size=64, ctx_range=(1280, 2560), stride=2560),
+    dict(batch=160, next_n=2, heads=32, page_size=16, ctx_range=(1200, 3200), stride=3200),
+    dict(batch=130, next_n=4, heads=16, page_size=128, ctx_range=(2000, 4032), stride=4032,
+         zero_every=10),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FLAT)))
+def test_flat_geometry_two_item_shares(gpu_lib, case):
+    """Decode shapes launched on the flat geometry (every row of a request in
+    one wave, at most 8192 possible iterations), every row against the oracle."""
+    kw = dict(FLAT[case])
+    stride = kw.pop("stride")
+    ps = kw["page_size"]
+    wl = synth.build_workload(f"flat{case}", head_dim=128, table="permuted", topk=512,
+                              seed=11 + case, table_width=-(-stride // ps), **kw)
+    wl.out_row_stride = stride
+    max_iters = wl.batch * (-(-min(wl.block_tables.shape[1] * ps, stride) // 64))
+    items = int(sum(-(-int(c) // 64) for c in wl.context_lens))
+    assert wl.heads * wl.next_n <= 64 and max_iters <= 8192 and items > 4096
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d, label=f"items={items}")
+    ref = oracle_rows(wl)
+    worst = check_rows(wl, out, ref)
+    say(f"flat case {case}: {items} items, worst rel err {worst:.3e}")
+    idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+    check_topk(idx, ref, wl.topk)
+
+
 def test_randomized_small_workloads(gpu_lib):
     """Seeded random shapes across every axis the kernels dispatch on (heads,
     next_n, page size, batch, context mix incl. zeros, output stride, table
