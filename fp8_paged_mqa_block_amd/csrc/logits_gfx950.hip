@@ -81,9 +81,14 @@ constexpr int kMaxPages = kIterTokens;                    // page ids per iterat
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// A lane's 32 bytes of one 128-byte q row or K record as an MFMA operand:
+// the 16 bytes at p and the 16 at p + 64 (p = row + 16*kq).  The matrix
+// core's K order only has to agree between q and K; this one reads each row
+// as two 64-byte halves (the four lanes of a row read one contiguous half per
+// load) and keeps K's LDS reads at the same bank spread.
 __device__ __forceinline__ v8i load_q32(const uint8_t* p) {
-  const u32x4* v = reinterpret_cast<const u32x4*>(p);  // 32-byte aligned
-  u32x4 a = v[0], b = v[1];
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 64);
   v8i r;
   r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
   r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
@@ -250,8 +255,128 @@ __device__ __forceinline__ void load_q(const LogitsParams& p, int b, int j0, int
     const float* wrow = p.w + row * H;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      qr.qa[jj][ht] = load_q32(qrow + (ht * 16 + m) * kHeadDim + kq * 32);
+      qr.qa[jj][ht] = load_q32(qrow + (ht * 16 + m) * kHeadDim + kq * 16);
       qr.wv[jj][ht] = *reinterpret_cast<const v4f*>(wrow + ht * 16 + kq * 4);
+    }
+  }
+}
+
+// q rows of request b loaded as whole lines: load i of a row moves its bytes
+// [1024 i, 1024 i + 1024) (heads 8i .. 8i+7), lane l taking the 16 bytes at
+// 16 l, so that every load reads 8 full 128-byte lines (load_q's operand-
+// shaped loads read 16 half lines each, and the memory pipeline counts
+// lines); assemble_q then builds the operands with cross-lane reads.  The
+// weights are loaded as load_q does.
+template <int H, int JW>
+struct QLines {
+  u32x4 v[JW][H / 8];
+};
+
+template <int H, int JW>
+__device__ __forceinline__ void load_q_lines(const LogitsParams& p, int b, int lane, int kq,
+                                             QLines<H, JW>& ql, QRegs<H, JW>& qr) {
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) {
+    const int j = min(jj, p.next_n - 1);  // rows past next_n are never stored
+    const int64_t row = (int64_t)b * p.next_n + j;
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + row * (int64_t)(H * kHeadDim)) + lane;
+    const float* wrow = p.w + row * H;
+#pragma unroll
+    for (int i = 0; i < H / 8; ++i) ql.v[jj][i] = src[64 * i];
+#pragma unroll
+    for (int ht = 0; ht < H / 16; ++ht)
+      qr.wv[jj][ht] = *reinterpret_cast<const v4f*>(wrow + ht * 16 + kq * 4);
+  }
+}
+
+// The MFMA operands from whole-line q loads by cross-lane reads, for a wave
+// whose gather is still in flight (the slot is busy): lane (m, kq) of head
+// tile ht needs bytes [16kq, 16kq+16) and [64+16kq, 64+16kq+16) of head
+// 16 ht + m, which load 2 ht + m/8 holds in lanes 8 (m%8) + kq and
+// 8 (m%8) + kq + 4.  A cross-lane read takes one register of every source
+// lane, so each dword is read from both loads of the tile and the lane keeps
+// the one of its head.  Only the q loads are waited for (the compiler counts
+// the gather's loads issued after them), so this overlaps the gather.
+template <int H, int JW>
+__device__ __forceinline__ void assemble_q_xlane(const QLines<H, JW>& ql, int lane,
+                                                 QRegs<H, JW>& qr) {
+  const int m = lane & 15, kq = lane >> 4;
+  const int a0 = (8 * (m & 7) + kq) * 4;  // byte index of the source lane
+  const int a1 = a0 + 16;
+  const bool low = m < 8;
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) {
+#pragma unroll
+    for (int ht = 0; ht < H / 16; ++ht) {
+      const u32x4 A = ql.v[jj][2 * ht], B = ql.v[jj][2 * ht + 1];
+      u32x4 x0, y0, x1, y1;
+      // Inline assembly with its own LDS-counter wait on purpose: the compiler
+      // drains every in-flight LDS-bound load before any LDS instruction it
+      // emits (it cannot tell that a cross-lane read touches no LDS memory),
+      // which would wait for the gather
+      asm volatile(
+          "ds_bpermute_b32 %0, %16, %18\n\t"
+          "ds_bpermute_b32 %1, %16, %19\n\t"
+          "ds_bpermute_b32 %2, %16, %20\n\t"
+          "ds_bpermute_b32 %3, %16, %21\n\t"
+          "ds_bpermute_b32 %4, %16, %22\n\t"
+          "ds_bpermute_b32 %5, %16, %23\n\t"
+          "ds_bpermute_b32 %6, %16, %24\n\t"
+          "ds_bpermute_b32 %7, %16, %25\n\t"
+          "ds_bpermute_b32 %8, %17, %18\n\t"
+          "ds_bpermute_b32 %9, %17, %19\n\t"
+          "ds_bpermute_b32 %10, %17, %20\n\t"
+          "ds_bpermute_b32 %11, %17, %21\n\t"
+          "ds_bpermute_b32 %12, %17, %22\n\t"
+          "ds_bpermute_b32 %13, %17, %23\n\t"
+          "ds_bpermute_b32 %14, %17, %24\n\t"
+          "ds_bpermute_b32 %15, %17, %25\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x0[0]), "=&v"(x0[1]), "=&v"(x0[2]), "=&v"(x0[3]), "=&v"(y0[0]), "=&v"(y0[1]),
+            "=&v"(y0[2]), "=&v"(y0[3]), "=&v"(x1[0]), "=&v"(x1[1]), "=&v"(x1[2]), "=&v"(x1[3]),
+            "=&v"(y1[0]), "=&v"(y1[1]), "=&v"(y1[2]), "=&v"(y1[3])
+          : "v"(a0), "v"(a1), "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "v"(B[0]), "v"(B[1]),
+            "v"(B[2]), "v"(B[3]));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        qr.qa[jj][ht][c] = (int)(low ? x0[c] : y0[c]);
+        qr.qa[jj][ht][4 + c] = (int)(low ? x1[c] : y1[c]);
+      }
+    }
+  }
+}
+
+// The MFMA operands from whole-line q loads, through the wave's K slot once
+// the iteration's K operands have been read from it: the lines are written as
+// padded rows (head h of row jj at (jj*H + h) * 144 bytes; the flat geometry
+// holds at most 64 heads x rows, 9216 bytes), and lane (m, kq) of head tile
+// ht reads bytes [16kq, 16kq+16) and [64+16kq, 64+16kq+16) of head 16 ht + m
+// back, the 16 lanes of one kq on distinct banks as for the K operands.
+template <int H, int JW>
+__device__ __forceinline__ void assemble_q(const QLines<H, JW>& ql, int lane, uint8_t* slot,
+                                           QRegs<H, JW>& qr) {
+  static_assert(H * JW * kLdsRecord <= kSlotBytes, "q rows must fit the K slot");
+  const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) {
+#pragma unroll
+    for (int i = 0; i < H / 8; ++i) {
+      const int h = 8 * i + (lane >> 3);
+      *reinterpret_cast<u32x4*>(slot + (jj * H + h) * kLdsRecord + 16 * (lane & 7)) = ql.v[jj][i];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are written
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) {
+#pragma unroll
+    for (int ht = 0; ht < H / 16; ++ht) {
+      const uint8_t* r = slot + (jj * H + 16 * ht + m) * kLdsRecord + 16 * kq;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(r);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 64);
+      qr.qa[jj][ht][0] = lo[0]; qr.qa[jj][ht][1] = lo[1];
+      qr.qa[jj][ht][2] = lo[2]; qr.qa[jj][ht][3] = lo[3];
+      qr.qa[jj][ht][4] = hi[0]; qr.qa[jj][ht][5] = hi[1];
+      qr.qa[jj][ht][6] = hi[2]; qr.qa[jj][ht][7] = hi[3];
     }
   }
 }
@@ -393,6 +518,30 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
   }
 }
 
+// The gather of one iteration that lies in one page (pages of 64 tokens or
+// more), from that page's id: the same loads as issue_gather's page-sized
+// path.
+__device__ __forceinline__ void gather_page(const LogitsParams& p, int it, int64_t id, int lane,
+                                            const ChunkOffsets& co, uint8_t* slot) {
+  const int t0 = it * kIterTokens;
+  const uint8_t* src =
+      p.kv + id * p.page_bytes + (int32_t)((t0 & (p.page_size - 1)) * kRecordBytes);
+#pragma unroll
+  for (int i = 0; i < kGatherLoads; ++i)
+    __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
+}
+
+// The page id of an iteration that lies in one page, by a scalar load (the
+// request and iteration are wave-uniform): it is tracked by the scalar memory
+// counter, so vector loads issued after it are not waited for when it is.
+__device__ __forceinline__ int64_t page_id(const LogitsParams& p, const Run& c) {
+  const int64_t idx =
+      (int64_t)uniform(c.b) * p.table_stride + ((uniform(c.it0) * kIterTokens) >> p.log2_page);
+  const __attribute__((address_space(4))) int64_t* t =
+      (const __attribute__((address_space(4))) int64_t*)p.tables;
+  return t[idx];
+}
+
 // Wait until at most n vector memory instructions are outstanding (n one of
 // the values the ring produces, a multiple of kGatherLoads below 4 of them;
 // anything smaller waits for all).
@@ -484,7 +633,8 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
 
 // The iteration's operands from its LDS slot (record x at x * 144, scale at
 // byte 140 of it): per tile, this lane's 32-byte B operand (token m of the
-// tile, value bytes 32*kq .. 32*kq+31) and that token's scale.  The 144-byte
+// tile, value bytes 16*kq .. 16*kq+15 and 64+16*kq .. 64+16*kq+15, the order
+// load_q32 gives q) and that token's scale.  The 144-byte
 // stride keeps the 16 lanes of one kq on distinct banks.  Inline assembly with
 // its own LDS wait on purpose: the compiler cannot tell which in-flight
 // LDS-bound loads a plain LDS read could alias and would drain every one of
@@ -501,19 +651,19 @@ __device__ __forceinline__ SlotOperands read_slot(const uint8_t* slot, int lane)
   const int m = lane & 15, kq = lane >> 4;
   const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)slot);
   // tile t's addresses are tile 0's plus t * 2304
-  const uint32_t av = base + (uint32_t)(m * kLdsRecord + 32 * kq);
+  const uint32_t av = base + (uint32_t)(m * kLdsRecord + 16 * kq);
   const uint32_t as = base + (uint32_t)(m * kLdsRecord + kLdsRecord - 4);
   u32x4 lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
   SlotOperands r;
   asm volatile(
       "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %1, %12 offset:16\n\t"
+      "ds_read_b128 %1, %12 offset:64\n\t"
       "ds_read_b128 %2, %12 offset:2304\n\t"
-      "ds_read_b128 %3, %12 offset:2320\n\t"
+      "ds_read_b128 %3, %12 offset:2368\n\t"
       "ds_read_b128 %4, %12 offset:4608\n\t"
-      "ds_read_b128 %5, %12 offset:4624\n\t"
+      "ds_read_b128 %5, %12 offset:4672\n\t"
       "ds_read_b128 %6, %12 offset:6912\n\t"
-      "ds_read_b128 %7, %12 offset:6928\n\t"
+      "ds_read_b128 %7, %12 offset:6976\n\t"
       "ds_read_b32 %8, %13\n\t"
       "ds_read_b32 %9, %13 offset:2304\n\t"
       "ds_read_b32 %10, %13 offset:4608\n\t"
@@ -692,43 +842,64 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
 // mostly consecutive iterations of one request, whose q rows stay in
 // registers, and consecutive waves on an XCD read the same q rows and table
 // lines from that XCD's L2.  One K slot per wave, refilled once its item is
-// scored; the page ids of the next item travel with the current gather.  The
+// scored.  Pages of 64 tokens or more hold a whole item: its page id comes by
+// a scalar load and q is requested before the gather; smaller pages stage the
+// item's page ids in LDS, and the next item's ids travel with the current
+// gather.  The
 // host takes this geometry only when the possible iterations are at most two
 // residencies, so a share holds one or two items.
-__device__ __forceinline__ void locate_item(const LogitsParams& p, uint32_t e, int lane,
-                                            uint32_t n0, int ctx0, uint32_t incl0,
-                                            uint32_t chunk0, Run& run) {
+// A one-iteration run: iteration it0 of request b (context ctx).  Built in one
+// place from plain values, so that no field is stored on one path and not on
+// another (such stores through a merged pointer keep the struct in scratch
+// memory).
+__device__ __forceinline__ Run item_run(const LogitsParams& p, int b, int ctx, int it0) {
+  Run r;
+  r.b = b;
+  r.ctx = ctx;
+  r.ctx_eff = min(ctx, p.max_tokens);
+  r.it0 = it0;
+  r.n_it = 1;
+  return r;
+}
+
+// Item e of the request-ordered list (e < the list's length).
+__device__ __forceinline__ Run locate_item(const LogitsParams& p, uint32_t e, int lane,
+                                           uint32_t n0, int ctx0, uint32_t incl0,
+                                           uint32_t chunk0) {
   uint32_t before = 0, n = n0, incl = incl0, chunk = chunk0;
   int ctx = ctx0;
-  for (int c0 = 0;;) {
+  int b = 0, bctx = 0, it0 = 0;
+  for (int c0 = 0; c0 < p.batch;) {
     if (before + chunk > e) {
       const uint64_t past = __ballot(before + incl > e);
       const int f = uniform(__builtin_ctzll(past));
-      run.b = c0 + f;
-      run.ctx = (int)lane_of((uint32_t)ctx, f);
-      run.ctx_eff = min(run.ctx, p.max_tokens);
-      run.it0 = (int)(e - (before + lane_of(incl, f) - lane_of(n, f)));
-      run.n_it = 1;
-      return;
+      b = c0 + f;
+      bctx = (int)lane_of((uint32_t)ctx, f);
+      it0 = (int)(e - (before + lane_of(incl, f) - lane_of(n, f)));
+      break;
     }
     before += chunk;
     c0 += 64;
-    if (c0 >= p.batch) return;  // not reached: the caller passes e < total
+    if (c0 >= p.batch) break;  // not reached: e lies inside the list
     n = (uint32_t)lane_iters(p, c0, lane, ctx);
     incl = wave_prefix(n, lane, chunk);
   }
+  return item_run(p, b, bctx, it0);
 }
 
-// The item after `cur`: its next iteration, or the first of a later request.
-__device__ __forceinline__ void next_item(const LogitsParams& p, const Run& cur, uint32_t e,
+// The item after `cur` (item e of the list): its next iteration, or the first
+// of a later request.
+__device__ __forceinline__ Run next_item(const LogitsParams& p, const Run& cur, uint32_t e,
                                          int lane, uint32_t n0, int ctx0, uint32_t incl0,
-                                         uint32_t chunk0, Run& nxt) {
-  if (cur.it0 + 1 < n_iters(cur.ctx, p.max_tokens)) {
-    nxt = cur;
-    nxt.it0 = cur.it0 + 1;
-  } else {
-    locate_item(p, e, lane, n0, ctx0, incl0, chunk0, nxt);
+                                         uint32_t chunk0) {
+  int b = cur.b, ctx = cur.ctx, it0 = cur.it0 + 1;
+  if (it0 >= n_iters(cur.ctx, p.max_tokens)) {
+    const Run r = locate_item(p, e, lane, n0, ctx0, incl0, chunk0);
+    b = r.b;
+    ctx = r.ctx;
+    it0 = r.it0;
   }
+  return item_run(p, b, ctx, it0);
 }
 
 template <int H, int JW>
@@ -762,24 +933,61 @@ void logits_flat_kernel(LogitsParams p) {
   uint32_t e = lo + k * a + min(k, r);
 
   // at most two items: the grid covers at least half of the possible ones
-  Run cur, nxt;
-  locate_item(p, e, lane, n0, ctx0, incl0, chunk0, cur);
+  Run cur = locate_item(p, e, lane, n0, ctx0, incl0, chunk0), nxt = cur;
+  QRegs<H, JW> qr;
+  QLines<H, JW> ql;
+  if (p.log2_page >= 6) {
+    // one page per item: its id comes by a scalar load, and q is requested
+    // right behind it as whole lines, ahead of this wave's gather (and of most
+    // waves'), then shaped into operands while the gather is in flight
+    const int64_t id0 = page_id(p, cur);
+    load_q_lines<H, JW>(p, cur.b, lane, kq, ql, qr);
+    gather_page(p, cur.it0, id0, lane, chunk_offsets(lane), slot);
+    // the q loads have landed once at most the gather's loads are left (the
+    // vector memory counter drains in order); the compiler would drain the
+    // gather too
+    __builtin_amdgcn_s_waitcnt(0x0f70 | kGatherLoads);  // vmcnt(kGatherLoads)
+    assemble_q_xlane<H, JW>(ql, lane, qr);
+    int64_t id1 = 0;
+    if (cnt > 1) {
+      nxt = next_item(p, cur, e + 1, lane, n0, ctx0, incl0, chunk0);
+      id1 = page_id(p, nxt);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the gather
+    score<H, JW>(p, cur, cur.it0, 0, lane, qr, slot);
+    if (cnt == 1) return;
+    // the slot reads are done (read_slot waits for them): refill it.  The next
+    // item's fields and the lane pass through empty asm so that its addresses
+    // are formed here, not early and spilled: a spill reload between the
+    // gather's loads would wait for every load issued before it.
+    int l2 = lane;
+    nxt.it0 = uniform(nxt.it0);
+    nxt.b = uniform(nxt.b);
+    asm volatile("" : "+v"(l2), "+s"(nxt.it0), "+s"(nxt.b));
+    gather_page(p, nxt.it0, id1, l2, chunk_offsets(l2), slot);
+    // a second item's q (few waves have one) takes the operand-shaped loads,
+    // which need no registers beside the operands
+    if (nxt.b != cur.b) load_q<H, JW>(p, nxt.b, 0, m, kq, qr);
+    __builtin_amdgcn_s_waitcnt(0);
+    score<H, JW>(p, nxt, nxt.it0, 0, lane, qr, slot);
+    return;
+  }
+  // smaller pages: the item's page ids are staged in LDS, one per lane
   issue_ids(p, cur, cur.it0, lane, ids[0]);
   __builtin_amdgcn_s_waitcnt(0);  // page ids in LDS
   issue_gather(p, cur.it0, cur.ctx_eff, ids[0], lane, chunk_offsets(lane), slot);
   if (cnt > 1) {
-    next_item(p, cur, e + 1, lane, n0, ctx0, incl0, chunk0, nxt);
+    nxt = next_item(p, cur, e + 1, lane, n0, ctx0, incl0, chunk0);
     issue_ids(p, nxt, nxt.it0, lane, ids[1]);
   }
-  QRegs<H, JW> qr;
-  load_q<H, JW>(p, cur.b, 0, m, kq, qr);
+  load_q_lines<H, JW>(p, cur.b, lane, kq, ql, qr);
   __builtin_amdgcn_s_waitcnt(0);  // the gather, q and the next item's ids
-  score<H, JW>(p, cur, cur.it0, 0, lane, qr, slot);
+  {
+    const SlotOperands op = read_slot(slot, lane);
+    assemble_q<H, JW>(ql, lane, slot, qr);
+    score_ops<H, JW>(p, cur, cur.it0, 0, lane, qr, op);
+  }
   if (cnt == 1) return;
-  // the slot reads are done (read_slot waits for them): refill it.  The next
-  // item's fields and the lane pass through empty asm so that its addresses
-  // are formed here, not early and spilled: a spill reload between the
-  // gather's loads would wait for every load issued before it.
   int l2 = lane;
   nxt.it0 = uniform(nxt.it0);
   nxt.ctx_eff = uniform(nxt.ctx_eff);
