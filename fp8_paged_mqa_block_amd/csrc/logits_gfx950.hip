@@ -942,6 +942,7 @@ void logits_flat_kernel(LogitsParams p) {
     // waves'), then shaped into operands while the gather is in flight
     const int64_t id0 = page_id(p, cur);
     load_q_lines<H, JW>(p, cur.b, lane, kq, ql, qr);
+    asm volatile("" ::: "memory");  // every q load is issued before the gather
     gather_page(p, cur.it0, id0, lane, chunk_offsets(lane), slot);
     // the q loads have landed once at most the gather's loads are left (the
     // vector memory counter drains in order); the compiler would drain the
