@@ -159,20 +159,30 @@ struct Run {
   int b, ctx, ctx_eff, it0, n_it;
 };
 
+// What a wave needs first: the context lengths, the batch and the grid's
+// token bound.  The kernels take them as their leading scalar arguments, which
+// the dispatch preloads into SGPRs (the build asks for 8 preloaded dwords), so
+// the context-length loads issue without waiting for the argument block.
+struct CtxArgs {
+  const int32_t* ctx;
+  int32_t batch;
+  int32_t max_tokens;
+};
+
 // Iterations of request c0 + lane (0 past the batch), and its context length.
-__device__ __forceinline__ int lane_iters(const LogitsParams& p, int c0, int lane, int& ctx) {
+__device__ __forceinline__ int lane_iters(const CtxArgs& a, int c0, int lane, int& ctx) {
   const int b = c0 + lane;
-  ctx = b < p.batch ? max(p.ctx[b], 0) : 0;
-  return n_iters(ctx, p.max_tokens);
+  ctx = b < a.batch ? max(a.ctx[b], 0) : 0;
+  return n_iters(ctx, a.max_tokens);
 }
 
 // Runs needed when no run is longer than P iterations: sum over the batch of
 // ceil(n_b / P).
-__device__ uint64_t runs_for(const LogitsParams& p, int lane, uint32_t n_first, uint32_t P) {
+__device__ uint64_t runs_for(const CtxArgs& a, int lane, uint32_t n_first, uint32_t P) {
   uint64_t runs = wave_sum(ceil_div(n_first, P));
-  for (int c0 = 64; c0 < p.batch; c0 += 64) {
+  for (int c0 = 64; c0 < a.batch; c0 += 64) {
     int ctx;
-    runs += wave_sum(ceil_div((uint32_t)lane_iters(p, c0, lane, ctx), P));
+    runs += wave_sum(ceil_div((uint32_t)lane_iters(a, c0, lane, ctx), P));
   }
   return runs;
 }
@@ -184,35 +194,35 @@ __device__ uint64_t runs_for(const LogitsParams& p, int lane, uint32_t n_first, 
 // in request order; units past the last run have nothing to do.  Each wave
 // computes the split itself from the context lengths, so the host never reads
 // them.
-__device__ bool find_run(const LogitsParams& p, int unit, int lane, Run& run) {
+__device__ bool find_run(const CtxArgs& a, const LogitsParams& p, int unit, int lane, Run& run) {
   int ctx0;
-  const uint32_t n0 = (uint32_t)lane_iters(p, 0, lane, ctx0);
+  const uint32_t n0 = (uint32_t)lane_iters(a, 0, lane, ctx0);
   uint64_t total = wave_sum(n0);
   uint32_t nmax = wave_max(n0);
-  for (int c0 = 64; c0 < p.batch; c0 += 64) {
+  for (int c0 = 64; c0 < a.batch; c0 += 64) {
     int ctx;
-    const uint32_t n = (uint32_t)lane_iters(p, c0, lane, ctx);
+    const uint32_t n = (uint32_t)lane_iters(a, c0, lane, ctx);
     total += wave_sum(n);
     nmax = max(nmax, wave_max(n));
   }
   if (total == 0) return false;
   const uint32_t slices = (uint32_t)p.n_slices;
   uint32_t P = (uint32_t)((total + slices - 1) / slices);
-  if (runs_for(p, lane, n0, P) > slices) {
+  if (runs_for(a, lane, n0, P) > slices) {
     // runs_for(lo) > slices >= runs_for(hi): bisect for the smallest fit
     uint32_t lo = P, hi = nmax;
     while (hi - lo > 1u) {
       const uint32_t mid = lo + (hi - lo) / 2u;
-      if (runs_for(p, lane, n0, mid) <= slices) hi = mid;
+      if (runs_for(a, lane, n0, mid) <= slices) hi = mid;
       else lo = mid;
     }
     P = hi;
   }
   // locate unit: the request whose runs cover it
   uint32_t before = 0;
-  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+  for (int c0 = 0; c0 < a.batch; c0 += 64) {
     int ctx = ctx0;
-    const uint32_t n = c0 == 0 ? n0 : (uint32_t)lane_iters(p, c0, lane, ctx);
+    const uint32_t n = c0 == 0 ? n0 : (uint32_t)lane_iters(a, c0, lane, ctx);
     const uint32_t c = ceil_div(n, P);
     uint32_t chunk_runs;
     const uint32_t incl = wave_prefix(c, lane, chunk_runs);
@@ -223,7 +233,7 @@ __device__ bool find_run(const LogitsParams& p, int unit, int lane, Run& run) {
       const uint32_t i = (uint32_t)unit - (before + lane_of(incl, f) - c_f);
       run.b = c0 + f;
       run.ctx = (int)lane_of((uint32_t)ctx, f);
-      run.ctx_eff = min(run.ctx, p.max_tokens);
+      run.ctx_eff = min(run.ctx, a.max_tokens);
       run.it0 = (int)((uint64_t)n_f * i / c_f);
       run.n_it = (int)((uint64_t)n_f * (i + 1u) / c_f) - run.it0;
       return true;
@@ -730,7 +740,10 @@ __device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int i
 // memory counter drains in order) also proves they have landed.  Ids of
 // iteration j live in id slot j % 2R, values in ring slot j % R.
 template <int H, int JW, int WAVES, int RING>
-__global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
+__global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __restrict__ ctx_lens,
+                                                            int32_t batch, int32_t max_tokens,
+                                                            LogitsParams p) {
+  const CtxArgs ca{ctx_lens, batch, max_tokens};
   __shared__ __attribute__((aligned(16))) uint8_t ring[WAVES][RING][kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint32_t ids[WAVES][2 * RING][kMaxPages];
   const int lane = threadIdx.x & 63;
@@ -764,7 +777,7 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
       __builtin_amdgcn_global_load_lds(p.q + qline * 128, LDS_PTR(my_ring + 256), 4, 0, 0);
   }
   Run run;
-  if (wave >= (uint32_t)p.n_slices * (uint32_t)p.n_rgroups || !find_run(p, unit, lane, run)) {
+  if (wave >= (uint32_t)p.n_slices * (uint32_t)p.n_rgroups || !find_run(ca, p, unit, lane, run)) {
     __builtin_amdgcn_s_waitcnt(0);  // the warm-up loads write this workgroup's LDS: land them first
     return;
   }
@@ -852,24 +865,24 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(LogitsParams p) {
 // place from plain values, so that no field is stored on one path and not on
 // another (such stores through a merged pointer keep the struct in scratch
 // memory).
-__device__ __forceinline__ Run item_run(const LogitsParams& p, int b, int ctx, int it0) {
+__device__ __forceinline__ Run item_run(const CtxArgs& a, int b, int ctx, int it0) {
   Run r;
   r.b = b;
   r.ctx = ctx;
-  r.ctx_eff = min(ctx, p.max_tokens);
+  r.ctx_eff = min(ctx, a.max_tokens);
   r.it0 = it0;
   r.n_it = 1;
   return r;
 }
 
 // Item e of the request-ordered list (e < the list's length).
-__device__ __forceinline__ Run locate_item(const LogitsParams& p, uint32_t e, int lane,
+__device__ __forceinline__ Run locate_item(const CtxArgs& a, uint32_t e, int lane,
                                            uint32_t n0, int ctx0, uint32_t incl0,
                                            uint32_t chunk0) {
   uint32_t before = 0, n = n0, incl = incl0, chunk = chunk0;
   int ctx = ctx0;
   int b = 0, bctx = 0, it0 = 0;
-  for (int c0 = 0; c0 < p.batch;) {
+  for (int c0 = 0; c0 < a.batch;) {
     if (before + chunk > e) {
       const uint64_t past = __ballot(before + incl > e);
       const int f = uniform(__builtin_ctzll(past));
@@ -880,31 +893,33 @@ __device__ __forceinline__ Run locate_item(const LogitsParams& p, uint32_t e, in
     }
     before += chunk;
     c0 += 64;
-    if (c0 >= p.batch) break;  // not reached: e lies inside the list
-    n = (uint32_t)lane_iters(p, c0, lane, ctx);
+    if (c0 >= a.batch) break;  // not reached: e lies inside the list
+    n = (uint32_t)lane_iters(a, c0, lane, ctx);
     incl = wave_prefix(n, lane, chunk);
   }
-  return item_run(p, b, bctx, it0);
+  return item_run(a, b, bctx, it0);
 }
 
 // The item after `cur` (item e of the list): its next iteration, or the first
 // of a later request.
-__device__ __forceinline__ Run next_item(const LogitsParams& p, const Run& cur, uint32_t e,
+__device__ __forceinline__ Run next_item(const CtxArgs& a, const Run& cur, uint32_t e,
                                          int lane, uint32_t n0, int ctx0, uint32_t incl0,
                                          uint32_t chunk0) {
   int b = cur.b, ctx = cur.ctx, it0 = cur.it0 + 1;
-  if (it0 >= n_iters(cur.ctx, p.max_tokens)) {
-    const Run r = locate_item(p, e, lane, n0, ctx0, incl0, chunk0);
+  if (it0 >= n_iters(cur.ctx, a.max_tokens)) {
+    const Run r = locate_item(a, e, lane, n0, ctx0, incl0, chunk0);
     b = r.b;
     ctx = r.ctx;
     it0 = r.it0;
   }
-  return item_run(p, b, ctx, it0);
+  return item_run(a, b, ctx, it0);
 }
 
 template <int H, int JW>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void logits_flat_kernel(LogitsParams p) {
+void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t max_tokens,
+                        LogitsParams p) {
+  const CtxArgs ca{ctx_lens, batch, max_tokens};
   __shared__ __attribute__((aligned(16))) uint8_t slot[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint32_t ids[2][kMaxPages];
   const int lane = threadIdx.x;
@@ -915,13 +930,13 @@ void logits_flat_kernel(LogitsParams p) {
   const uint32_t kx = gridDim.x >> 3;  // waves per XCD
   // iterations of every request
   int ctx0;
-  const uint32_t n0 = (uint32_t)lane_iters(p, 0, lane, ctx0);
+  const uint32_t n0 = (uint32_t)lane_iters(ca, 0, lane, ctx0);
   uint32_t chunk0;
   const uint32_t incl0 = wave_prefix(n0, lane, chunk0);
   uint32_t total = chunk0;
-  for (int c0 = 64; c0 < p.batch; c0 += 64) {
+  for (int c0 = 64; c0 < ca.batch; c0 += 64) {
     int ctx;
-    total += wave_sum((uint32_t)lane_iters(p, c0, lane, ctx));
+    total += wave_sum((uint32_t)lane_iters(ca, c0, lane, ctx));
   }
   // this wave's share: items [e, e + cnt) of the list
   const uint32_t per = (total + 7u) >> 3;
@@ -933,7 +948,7 @@ void logits_flat_kernel(LogitsParams p) {
   uint32_t e = lo + k * a + min(k, r);
 
   // at most two items: the grid covers at least half of the possible ones
-  Run cur = locate_item(p, e, lane, n0, ctx0, incl0, chunk0), nxt = cur;
+  Run cur = locate_item(ca, e, lane, n0, ctx0, incl0, chunk0), nxt = cur;
   QRegs<H, JW> qr;
   QLines<H, JW> ql;
   if (p.log2_page >= 6) {
@@ -951,7 +966,7 @@ void logits_flat_kernel(LogitsParams p) {
     assemble_q_xlane<H, JW>(ql, lane, qr);
     int64_t id1 = 0;
     if (cnt > 1) {
-      nxt = next_item(p, cur, e + 1, lane, n0, ctx0, incl0, chunk0);
+      nxt = next_item(ca, cur, e + 1, lane, n0, ctx0, incl0, chunk0);
       id1 = page_id(p, nxt);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the gather
@@ -978,7 +993,7 @@ void logits_flat_kernel(LogitsParams p) {
   __builtin_amdgcn_s_waitcnt(0);  // page ids in LDS
   issue_gather(p, cur.it0, cur.ctx_eff, ids[0], lane, chunk_offsets(lane), slot);
   if (cnt > 1) {
-    nxt = next_item(p, cur, e + 1, lane, n0, ctx0, incl0, chunk0);
+    nxt = next_item(ca, cur, e + 1, lane, n0, ctx0, incl0, chunk0);
     issue_ids(p, nxt, nxt.it0, lane, ids[1]);
   }
   load_q_lines<H, JW>(p, cur.b, lane, kq, ql, qr);
@@ -1033,9 +1048,10 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
       const uint32_t n_wg = 8u * (uint32_t)(per_xcd < 16 * 32 ? per_xcd : 16 * 32);
       auto kern = logits_flat_kernel<H, JW>;
       if (tm.start || tm.stop)
-        hipExtLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, tm.start, tm.stop, 0, p);
+        hipExtLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, tm.start, tm.stop, 0, p.ctx,
+                              p.batch, p.max_tokens, p);
       else
-        hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, p);
+        hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, p.ctx, p.batch, p.max_tokens, p);
       return hipGetLastError();
     }
   }
@@ -1045,9 +1061,10 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
   auto kern = logits_kernel<H, JW, G::kWaves, G::kRingDepth>;
   if (tm.start || tm.stop)
     hipExtLaunchKernelGGL(kern, dim3(n_wg), dim3(64 * G::kWaves), 0, stream, tm.start, tm.stop, 0,
-                          p);
+                          p.ctx, p.batch, p.max_tokens, p);
   else
-    hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64 * G::kWaves), 0, stream, p);
+    hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64 * G::kWaves), 0, stream, p.ctx, p.batch,
+                       p.max_tokens, p);
   return hipGetLastError();
 }
 

@@ -392,26 +392,32 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
+// The row pointer, stride, context lengths and next_n come first as scalar
+// arguments: the dispatch preloads them into SGPRs (the build asks for 8
+// preloaded dwords), so the row and context-length loads issue at once.
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ logits,
+                                                       int64_t row_stride,
+                                                       const int32_t* __restrict__ ctx_lens,
+                                                       int32_t next_n, TopkParams p) {
   __shared__ TopkShared sh;
 
   const int r = blockIdx.x;
-  const int b = r / p.next_n;
-  const int j = r - b * p.next_n;
-  const float* row = p.logits + (int64_t)r * p.row_stride;
+  const int b = r / next_n;
+  const int j = r - b * next_n;
+  const float* row = logits + (int64_t)r * row_stride;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // When the row's stride spans the first size class, its scores are loaded
   // before the row length is known, so that the context-length read and this
   // load overlap instead of running back to back; rows of another class
   // discard them.
-  const bool early = p.row_stride >= (int64_t)kThreads * kSmallKeys;
+  const bool early = row_stride >= (int64_t)kThreads * kSmallKeys;
   const int64_t base_small = (int64_t)wave * 64 * kSmallKeys + lane;
   Chunk<kSmallKeys> first;
   if (early) first.load_span(row, base_small);
 
-  const int ctx = max(p.ctx[b], 0);
-  int n = min(max(ctx - p.next_n + j + 1, 0), ctx);
-  if ((int64_t)n > p.row_stride) n = (int)p.row_stride;
+  const int ctx = max(ctx_lens[b], 0);
+  int n = min(max(ctx - next_n + j + 1, 0), ctx);
+  if ((int64_t)n > row_stride) n = (int)row_stride;
   const int k = p.k;
   int32_t* out = p.out_idx + (int64_t)r * k;
 
@@ -439,9 +445,10 @@ hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t 
   const uint32_t rows = (uint32_t)p.batch * (uint32_t)p.next_n;
   if (tm.start || tm.stop)
     hipExtLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, tm.start, tm.stop,
-                          0, p);
+                          0, p.logits, p.row_stride, p.ctx, p.next_n, p);
   else
-    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, p.logits, p.row_stride,
+                       p.ctx, p.next_n, p);
   return hipGetLastError();
 }
 
