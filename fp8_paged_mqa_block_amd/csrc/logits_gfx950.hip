@@ -918,7 +918,7 @@ __device__ __forceinline__ Run next_item(const CtxArgs& a, const Run& cur, uint3
 template <int H, int JW>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t max_tokens,
-                        LogitsParams p) {
+                        const int64_t* __restrict__ tables, int32_t warm_lines, LogitsParams p) {
   const CtxArgs ca{ctx_lens, batch, max_tokens};
   __shared__ __attribute__((aligned(16))) uint8_t slot[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint32_t ids[2][kMaxPages];
@@ -928,6 +928,16 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   const uint32_t xcd = blockIdx.x & 7u;
   const uint32_t k = blockIdx.x >> 3;
   const uint32_t kx = gridDim.x >> 3;  // waves per XCD
+  // while the context lengths are read: a small block table is pulled into
+  // this XCD's L2 (one 4-byte load per 128-byte line, into the idle K slot;
+  // the gather that fills the slot later lands after it), so that the page-id
+  // load that follows the item search hits L2
+  {
+    const int64_t line = (int64_t)k * 64 + lane;
+    if (line < warm_lines)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(tables) + line * 128,
+                                       LDS_PTR(slot), 4, 0, 0);
+  }
   // iterations of every request
   int ctx0;
   const uint32_t n0 = (uint32_t)lane_iters(ca, 0, lane, ctx0);
@@ -944,7 +954,10 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   const uint32_t nx = min(lo + per, total) - lo;
   const uint32_t a = nx / kx, r = nx % kx;
   const uint32_t cnt = a + (k < r ? 1u : 0u);
-  if (cnt == 0) return;
+  if (cnt == 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // the warm-up load writes this workgroup's LDS
+    return;
+  }
   uint32_t e = lo + k * a + min(k, r);
 
   // at most two items: the grid covers at least half of the possible ones
@@ -1047,11 +1060,13 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
       const int64_t per_xcd = (p.flat_items + 7) / 8;
       const uint32_t n_wg = 8u * (uint32_t)(per_xcd < 16 * 32 ? per_xcd : 16 * 32);
       auto kern = logits_flat_kernel<H, JW>;
+      const int32_t warm = (int32_t)p.warm_table_lines;  // at most 8192 (a 1 MiB table)
       if (tm.start || tm.stop)
         hipExtLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, tm.start, tm.stop, 0, p.ctx,
-                              p.batch, p.max_tokens, p);
+                              p.batch, p.max_tokens, p.tables, warm, p);
       else
-        hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, p.ctx, p.batch, p.max_tokens, p);
+        hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, p.ctx, p.batch, p.max_tokens,
+                           p.tables, warm, p);
       return hipGetLastError();
     }
   }
