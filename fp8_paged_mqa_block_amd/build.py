@@ -23,10 +23,10 @@ FLAGS = [
     "-fvisibility=hidden",  # only the C ABI (PMQA_API) is exported
     # packed fp32 VALU forms stay off: the compiler may not form v_pk_*_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # the kernels' leading scalar arguments (context lengths, batch, bounds) are
-    # preloaded into SGPRs by the dispatch, so a wave's first loads need not
-    # wait for the argument block
-    "-mllvm", "-amdgpu-kernarg-preload-count=8",
+    # the kernels' leading scalar arguments (context lengths, batch, bounds,
+    # the tables and q to warm) are preloaded into SGPRs by the dispatch, so a
+    # wave's first loads need not wait for the argument block
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

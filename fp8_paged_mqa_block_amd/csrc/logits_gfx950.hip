@@ -161,7 +161,7 @@ struct Run {
 
 // What a wave needs first: the context lengths, the batch and the grid's
 // token bound.  The kernels take them as their leading scalar arguments, which
-// the dispatch preloads into SGPRs (the build asks for 8 preloaded dwords), so
+// the dispatch preloads into SGPRs (the build asks for up to 16 dwords), so
 // the context-length loads issue without waiting for the argument block.
 struct CtxArgs {
   const int32_t* ctx;
@@ -918,7 +918,8 @@ __device__ __forceinline__ Run next_item(const CtxArgs& a, const Run& cur, uint3
 template <int H, int JW>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t max_tokens,
-                        const int64_t* __restrict__ tables, int32_t warm_lines, LogitsParams p) {
+                        const int64_t* __restrict__ tables, int32_t warm_lines,
+                        const uint8_t* __restrict__ q, int32_t q_lines, LogitsParams p) {
   const CtxArgs ca{ctx_lens, batch, max_tokens};
   __shared__ __attribute__((aligned(16))) uint8_t slot[kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint32_t ids[2][kMaxPages];
@@ -929,14 +930,19 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   const uint32_t k = blockIdx.x >> 3;
   const uint32_t kx = gridDim.x >> 3;  // waves per XCD
   // while the context lengths are read: a small block table is pulled into
-  // this XCD's L2 (one 4-byte load per 128-byte line, into the idle K slot;
-  // the gather that fills the slot later lands after it), so that the page-id
-  // load that follows the item search hits L2
+  // this XCD's L2, and so is the eighth of a small q that this XCD's share of
+  // the request-ordered items mostly needs (one 4-byte load per 128-byte line,
+  // into the idle K slot; the gather that fills the slot later lands after
+  // them), so that the page-id and q loads that follow the item search hit L2
   {
     const int64_t line = (int64_t)k * 64 + lane;
     if (line < warm_lines)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(tables) + line * 128,
                                        LDS_PTR(slot), 4, 0, 0);
+    const int32_t q8 = (q_lines + 7) >> 3;
+    const int64_t ql = (int64_t)xcd * q8 + line;
+    if (line < q8 && ql < q_lines)
+      __builtin_amdgcn_global_load_lds(q + ql * 128, LDS_PTR(slot + 256), 4, 0, 0);
   }
   // iterations of every request
   int ctx0;
@@ -1061,12 +1067,13 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
       const uint32_t n_wg = 8u * (uint32_t)(per_xcd < 16 * 32 ? per_xcd : 16 * 32);
       auto kern = logits_flat_kernel<H, JW>;
       const int32_t warm = (int32_t)p.warm_table_lines;  // at most 8192 (a 1 MiB table)
+      const int32_t warm_q = (int32_t)p.warm_q_lines;    // at most 32768 (a 4 MiB q)
       if (tm.start || tm.stop)
         hipExtLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, tm.start, tm.stop, 0, p.ctx,
-                              p.batch, p.max_tokens, p.tables, warm, p);
+                              p.batch, p.max_tokens, p.tables, warm, p.q, warm_q, p);
       else
         hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, p.ctx, p.batch, p.max_tokens,
-                           p.tables, warm, p);
+                           p.tables, warm, p.q, warm_q, p);
       return hipGetLastError();
     }
   }

@@ -393,8 +393,8 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
 }
 
 // The row pointer, stride, context lengths and next_n come first as scalar
-// arguments: the dispatch preloads them into SGPRs (the build asks for 8
-// preloaded dwords), so the row and context-length loads issue at once.
+// arguments: the dispatch preloads them into SGPRs (the build asks for up to
+// 16 preloaded dwords), so the row and context-length loads issue at once.
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ logits,
                                                        int64_t row_stride,
                                                        const int32_t* __restrict__ ctx_lens,
