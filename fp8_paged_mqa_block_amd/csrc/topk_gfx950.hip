@@ -24,7 +24,9 @@
 //    address;
 //  * the passes stop as soon as the threshold bin is taken whole, or holds at
 //    most 128 keys (256 for a streamed row, where a pass costs a full read):
-//    those are then gathered in row order and ranked against each other;
+//    those are then gathered in row order and ranked against each other,
+//    each candidate compared as one 64-bit value (key above inverted
+//    position) by 8 lanes (4 for a streamed row), so all 16 waves rank;
 //  * each pass has two barriers: after the histogram, and after the per-wave
 //    bin totals; sums, prefix sums and min/max inside a wave use DPP row
 //    operations and lane reads, not LDS shuffles;
@@ -50,7 +52,6 @@ constexpr int kSmallKeys = 8;           // keys per thread for rows up to 8192
 constexpr int kLargeKeys = 16;          // keys per thread (or per chunk) beyond
 constexpr int kCandCap = 256;           // threshold bins this small are ranked directly
 constexpr int kCandCapHeld = 128;       // the same, for rows held in registers
-constexpr int kRankBlock = 32;          // candidates read per ranking step
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -365,31 +366,35 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     run_e += te;
   });
   if (!rank_bin) return;
-  // rank of each gathered key among the bin's run_e (<= kCandCap) keys:
-  // larger keys first, equal keys in row order (their gather order)
-  __syncthreads();
+  // rank of each gathered key among the bin's nc keys: larger keys first,
+  // equal keys in row order (their gather order).  A candidate compares as one
+  // 64-bit value, its key above its inverted position, so that one unsigned
+  // comparison orders both; the slots from nc to the cap hold key 0, whose
+  // values stay below every gathered key's (their positions come later).
+  // T consecutive lanes share a candidate, each comparing it with kCap / T
+  // slots, and add their counts, so every wave of the workgroup takes part.
+  constexpr int kCap = STREAM ? kCandCap : kCandCapHeld;
+  constexpr int T = kThreads / kCap;
+  constexpr int kPer = kCap / T;
+  static_assert(kCap * T == kThreads && kPer % 4 == 0 && (T & (T - 1)) == 0, "rank layout");
   const int nc = (int)run_e;
-  if (tid < nc) {
-    const uint32_t mine = sh.cand_key[tid];
-    int rank = 0;
-    // kRankBlock keys per step, all of a step's reads issued together; keys
-    // at or past nc (never written in this call) are not counted
-    for (int i0 = 0; i0 < nc; i0 += kRankBlock) {
-      uint4 o[kRankBlock / 4];
+  for (int i = nc + tid; i < kCap; i += kThreads) sh.cand_key[i] = 0u;
+  __syncthreads();
+  const int t = tid / T, part = tid % T;
+  const uint64_t mine = ((uint64_t)sh.cand_key[t] << 32) | (uint32_t)~(uint32_t)t;
+  uint32_t rank = 0;
 #pragma unroll
-      for (int u = 0; u < kRankBlock / 4; ++u)
-        o[u] = reinterpret_cast<const uint4*>(sh.cand_key)[(i0 >> 2) + u];
-#pragma unroll
-      for (int u = 0; u < kRankBlock / 4; ++u) {
-        const int i = i0 + 4 * u;
-        rank += (i < nc && (o[u].x > mine || (o[u].x == mine && i < tid))) ? 1 : 0;
-        rank += (i + 1 < nc && (o[u].y > mine || (o[u].y == mine && i + 1 < tid))) ? 1 : 0;
-        rank += (i + 2 < nc && (o[u].z > mine || (o[u].z == mine && i + 2 < tid))) ? 1 : 0;
-        rank += (i + 3 < nc && (o[u].w > mine || (o[u].w == mine && i + 3 < tid))) ? 1 : 0;
-      }
-    }
-    if (rank < remaining) out[first_eq + rank] = sh.cand_idx[tid];
+  for (int u = 0; u < kPer; u += 4) {
+    const int i = part * kPer + u;
+    const uint4 o = reinterpret_cast<const uint4*>(sh.cand_key)[i >> 2];
+    rank += ((((uint64_t)o.x << 32) | (uint32_t)~(uint32_t)i) > mine) ? 1u : 0u;
+    rank += ((((uint64_t)o.y << 32) | (uint32_t)~(uint32_t)(i + 1)) > mine) ? 1u : 0u;
+    rank += ((((uint64_t)o.z << 32) | (uint32_t)~(uint32_t)(i + 2)) > mine) ? 1u : 0u;
+    rank += ((((uint64_t)o.w << 32) | (uint32_t)~(uint32_t)(i + 3)) > mine) ? 1u : 0u;
   }
+#pragma unroll
+  for (int d = 1; d < T; d <<= 1) rank += (uint32_t)__shfl_xor((int)rank, d);
+  if (part == 0 && t < nc && rank < (uint32_t)remaining) out[first_eq + rank] = sh.cand_idx[t];
 }
 
 // The row pointer, stride, context lengths and next_n come first as scalar
