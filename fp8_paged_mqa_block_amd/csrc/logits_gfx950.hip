@@ -929,24 +929,42 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   const uint32_t xcd = blockIdx.x & 7u;
   const uint32_t k = blockIdx.x >> 3;
   const uint32_t kx = gridDim.x >> 3;  // waves per XCD
-  // while the context lengths are read: a small block table is pulled into
-  // this XCD's L2, and so is the eighth of a small q that this XCD's share of
-  // the request-ordered items mostly needs (one 4-byte load per 128-byte line,
+  // the context lengths of the first 64 requests are requested first, by one
+  // 4-byte LDS-bound load into the idle page-id slots (lanes past the batch
+  // reread the last one); then a small block table is pulled into this XCD's
+  // L2, and so is the eighth of a small q that this XCD's share of the
+  // request-ordered items mostly needs (one 4-byte load per 128-byte line,
   // into the idle K slot; the gather that fills the slot later lands after
-  // them), so that the page-id and q loads that follow the item search hit L2
+  // them), so that the page-id and q loads that follow the item search hit L2.
+  // The warm-up is exactly two loads (lanes without a line reread the first
+  // one), so vmcnt(2) proves the context lengths have landed without waiting
+  // for it: the counter drains in order, while a wait the compiler derived
+  // for a register load would also drain the warm-up.
+  __builtin_amdgcn_global_load_lds(ctx_lens + min(lane, batch - 1), LDS_PTR(&ids[1][0]), 4, 0, 0);
+  asm volatile("" ::: "memory");  // the context-length load goes first
   {
     const int64_t line = (int64_t)k * 64 + lane;
-    if (line < warm_lines)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(tables) + line * 128,
-                                       LDS_PTR(slot), 4, 0, 0);
+    const int64_t tl = line < warm_lines ? line : 0;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(tables) + tl * 128,
+                                     LDS_PTR(slot), 4, 0, 0);
     const int32_t q8 = (q_lines + 7) >> 3;
     const int64_t ql = (int64_t)xcd * q8 + line;
-    if (line < q8 && ql < q_lines)
-      __builtin_amdgcn_global_load_lds(q + ql * 128, LDS_PTR(slot + 256), 4, 0, 0);
+    const int64_t qq = line < q8 && ql < q_lines ? ql : 0;
+    __builtin_amdgcn_global_load_lds(q + qq * 128, LDS_PTR(slot + 256), 4, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70 | 2);  // vmcnt(2): the context lengths have landed
+  int craw;
+  {
+    // inline assembly with its own LDS wait, like the ring reads: a plain LDS
+    // read would make the compiler drain the warm-up loads first
+    const uint32_t ca_lds =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint32_t*)&ids[1][0]) +
+        4u * (uint32_t)lane;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(craw) : "v"(ca_lds) : "memory");
   }
   // iterations of every request
-  int ctx0;
-  const uint32_t n0 = (uint32_t)lane_iters(ca, 0, lane, ctx0);
+  const int ctx0 = lane < batch ? max(craw, 0) : 0;
+  const uint32_t n0 = (uint32_t)n_iters(ctx0, max_tokens);
   uint32_t chunk0;
   const uint32_t incl0 = wave_prefix(n0, lane, chunk0);
   uint32_t total = chunk0;
@@ -971,12 +989,14 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   QRegs<H, JW> qr;
   QLines<H, JW> ql;
   if (p.log2_page >= 6) {
-    // one page per item: its id comes by a scalar load, and q is requested
-    // right behind it as whole lines, ahead of this wave's gather (and of most
-    // waves'), then shaped into operands while the gather is in flight
-    const int64_t id0 = page_id(p, cur);
+    // one page per item: q is requested as whole lines, then the page id by a
+    // scalar load, ahead of this wave's gather (and of most waves'); q is
+    // shaped into operands while the gather is in flight
+    // (q first: waiting for a scalar load waits for all of them, and q's
+    // addresses come from scalar loads of the arguments)
     load_q_lines<H, JW>(p, cur.b, lane, kq, ql, qr);
     asm volatile("" ::: "memory");  // every q load is issued before the gather
+    const int64_t id0 = page_id(p, cur);
     gather_page(p, cur.it0, id0, lane, chunk_offsets(lane), slot);
     // the q loads have landed once at most the gather's loads are left (the
     // vector memory counter drains in order); the compiler would drain the
