@@ -979,7 +979,7 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   const uint32_t a = nx / kx, r = nx % kx;
   const uint32_t cnt = a + (k < r ? 1u : 0u);
   if (cnt == 0) {
-    __builtin_amdgcn_s_waitcnt(0);  // the warm-up load writes this workgroup's LDS
+    __builtin_amdgcn_s_waitcnt(0);  // the warm-up loads write this workgroup's LDS
     return;
   }
   uint32_t e = lo + k * a + min(k, r);
