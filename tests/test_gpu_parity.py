@@ -312,6 +312,25 @@ def test_topk_special_rows(gpu_lib):
             assert np.all(got[r, m:] == -1)
 
 
+@pytest.mark.parametrize("shape", [
+    dict(batch=5, next_n=1, heads=64, page_size=64),   # single-wave geometry, page-sized items
+    dict(batch=64, next_n=2, heads=32, page_size=8),   # single-wave geometry, small pages
+    dict(batch=5, next_n=3, heads=64, page_size=8),    # persistent geometry, 192-row units
+    dict(batch=3, next_n=1, heads=128, page_size=256),  # persistent geometry, 128-row units
+])
+def test_all_contexts_empty(gpu_lib, shape):
+    """A batch whose every context is empty: nothing is scored, every output
+    row keeps its sentinel, and the top-k rows are all -1."""
+    wl = synth.build_workload("empty", head_dim=128, table="permuted", topk=16, seed=5,
+                              context_lens=[0] * shape["batch"], **shape)
+    wl.out_row_stride = 512
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d, label="all empty")
+    check_untouched_rows(wl, out, range(wl.batch))
+    idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+    assert np.all(idx.cpu().numpy() == -1)
+
+
 @pytest.mark.parametrize("heads", [16, 32, 64, 128])
 def test_short_rows_meet_row_tolerance(gpu_lib, heads):
     """Rows that see only a few tokens, with sign-cancelling weights: the row's
