@@ -113,15 +113,12 @@ def pm_rows_per_wave(wl):
 
 
 def logits_kernel_name(wl):
-    """The logits kernel the library launches for this workload (the host's
-    choice of geometry: one wave per 64-token iteration while every row of a
-    request fits one wave and the grid bound is at most two residencies)."""
-    jw = pm_rows_per_wave(wl)
-    max_tokens = min(wl.block_tables.shape[1] * wl.page_size, wl.out_row_stride)
-    max_iters = wl.batch * ((max_tokens + 63) // 64)
-    if wl.heads * wl.next_n <= 64 and jw == wl.next_n and max_iters <= 2 * 16 * 256:
-        return f"logits_flat_kernel<{wl.heads},{jw}>"
-    return f"logits_kernel<{wl.heads},{jw}>"
+    """The logits kernel the library launches for this workload (asked of the
+    library itself, which takes the launch geometry from the same sizes)."""
+    import fp8_paged_mqa_block_amd as pm
+
+    return pm.logits_kernel(wl.batch, wl.next_n, wl.page_size, wl.out_row_stride, wl.heads,
+                            wl.block_tables.shape[1], head_dim=wl.head_dim)
 
 
 def measure_copy(dev, mib=512, reps=20):

@@ -18,6 +18,7 @@ __all__ = [
     "PmqaError",
     "load_library",
     "library_path",
+    "logits_kernel",
     "paged_mqa_logits",
     "topk_per_row",
     "check_inputs",
@@ -32,7 +33,7 @@ _lib: Optional[ctypes.CDLL] = None
 # Every symbol include/pmqa.h declares.
 EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "topk_per_row", "topk_per_row_timed",
            "pmqa_check_inputs", "quantize_k_cache", "quantize_k_cache_timed",
-           "pmqa_status_string", "pmqa_version")
+           "pmqa_status_string", "pmqa_version", "pmqa_logits_kernel")
 
 # pmqa_dtype codes of the K rows quantize_k_cache accepts
 _K_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
@@ -45,6 +46,17 @@ class PmqaError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn}: {_STATUS.get(status, status)} ({msg})")
         self.status = status
+
+
+def logits_kernel(batch: int, next_n: int, page_size: int, out_row_stride: int,
+                  num_heads: int, block_table_stride: int, head_dim: int = 128) -> str:
+    """Name of the logits kernel paged_mqa_logits launches for these sizes
+    (host only; see pmqa_logits_kernel in include/pmqa.h)."""
+    buf = ctypes.create_string_buffer(64)
+    st = load_library().pmqa_logits_kernel(batch, next_n, page_size, out_row_stride, num_heads,
+                                           head_dim, block_table_stride, buf, len(buf))
+    _check("pmqa_logits_kernel", st)
+    return buf.value.decode()
 
 
 def library_path() -> str:
@@ -80,6 +92,9 @@ def load_library() -> ctypes.CDLL:
     lib.pmqa_status_string.argtypes = [ctypes.c_int]
     lib.pmqa_version.restype = ctypes.c_int32
     lib.pmqa_version.argtypes = []
+    lib.pmqa_logits_kernel.restype = ctypes.c_int
+    lib.pmqa_logits_kernel.argtypes = [c_i32, c_i32, c_i32, c_i64, c_i32, c_i32, c_i64,
+                                       ctypes.c_char_p, c_i32]
     _lib = lib
     return lib
 

@@ -1127,6 +1127,13 @@ hipError_t launch_heads(const LogitsParams& p, int jw, const LaunchTiming& tm,
 }
 
 template <int H>
+int ring_depth(int jw) {
+  return jw <= 1 ? Geometry<H, 1>::kRingDepth
+                 : jw == 2 ? Geometry<H, 2>::kRingDepth
+                           : jw == 3 ? Geometry<H, 3>::kRingDepth : Geometry<H, 4>::kRingDepth;
+}
+
+template <int H>
 int waves_per_cu(int jw) {
   return jw <= 1 ? Geometry<H, 1>::kWaves
                  : jw == 2 ? Geometry<H, 2>::kWaves
@@ -1154,6 +1161,15 @@ LogitsShape logits_shape(int heads, int next_n) {
   // at most two residencies of 16 single-wave workgroups per CU
   sh.flat_max_items = heads * next_n <= 64 && sh.rows_per_wave == next_n ? 2 * 16 * 256 : 0;
   return sh;
+}
+
+void persistent_geometry(int heads, int rows_per_wave, int* waves, int* ring) {
+  switch (heads) {
+    case 16: *waves = waves_per_cu<16>(rows_per_wave); *ring = ring_depth<16>(rows_per_wave); break;
+    case 32: *waves = waves_per_cu<32>(rows_per_wave); *ring = ring_depth<32>(rows_per_wave); break;
+    case 64: *waves = waves_per_cu<64>(rows_per_wave); *ring = ring_depth<64>(rows_per_wave); break;
+    default: *waves = waves_per_cu<128>(rows_per_wave); *ring = ring_depth<128>(rows_per_wave); break;
+  }
 }
 
 hipError_t launch_logits(const LogitsParams& p, const LogitsShape& sh, int heads,

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
 
 #include "pmqa.h"
 #include "pmqa_internal.h"
@@ -20,6 +21,45 @@ int log2_exact(int64_t x) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The launch geometry of a logits call, from its sizes alone: the launch and
+// the name query both take it from here.
+struct LogitsPlan {
+  pmqa::LogitsShape sh;
+  int64_t max_tokens;  // the grid covers every token a request could have
+  int64_t max_iters;   // 64-token iterations the contexts could hold
+  int64_t n_rgroups;   // waves sharing a request's next_n rows
+  bool flat;           // one single-wave workgroup per iteration
+};
+
+LogitsPlan plan_logits(int32_t batch, int32_t next_n, int32_t page_size, int64_t out_row_stride,
+                       int32_t num_heads, int64_t block_table_stride) {
+  LogitsPlan pl;
+  // the table row's capacity and the output row's width bound a context
+  int64_t max_tokens = block_table_stride * (int64_t)page_size;
+  if (out_row_stride < max_tokens) max_tokens = out_row_stride;
+  if (max_tokens > INT32_MAX) max_tokens = INT32_MAX;
+  pl.max_tokens = max_tokens;
+  pl.sh = pmqa::logits_shape(num_heads, next_n);
+  pl.n_rgroups = (next_n + pl.sh.rows_per_wave - 1) / pl.sh.rows_per_wave;
+  pl.max_iters = (int64_t)batch * ((max_tokens + pl.sh.iter_tokens - 1) / pl.sh.iter_tokens);
+  pl.flat = pl.n_rgroups == 1 && pl.max_iters <= pl.sh.flat_max_items;
+  return pl;
+}
+
+// The host-checkable preconditions of a logits call's sizes (pointers aside).
+pmqa_status check_logits_sizes(int32_t batch, int32_t next_n, int32_t page_size,
+                               int64_t out_row_stride, int32_t num_heads, int32_t head_dim,
+                               int64_t block_table_stride) {
+  if (batch < 0 || next_n < 1 || out_row_stride < 1 || block_table_stride < 1)
+    return PMQA_ERR_SHAPE;
+  if (!valid_page_size(page_size)) return PMQA_ERR_SHAPE;
+  if (head_dim != pmqa::kHeadDim) return PMQA_ERR_UNSUPPORTED;
+  if (!(num_heads == 16 || num_heads == 32 || num_heads == 64 || num_heads == 128))
+    return PMQA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
+  return PMQA_OK;
+}
 
 }  // namespace
 
@@ -39,6 +79,27 @@ const char* pmqa_status_string(pmqa_status status) {
 
 int32_t pmqa_version(void) { return 100; }
 
+pmqa_status pmqa_logits_kernel(int32_t batch, int32_t next_n, int32_t page_size,
+                               int64_t out_row_stride, int32_t num_heads, int32_t head_dim,
+                               int64_t block_table_stride, char* name, int32_t name_len) {
+  if (!name || name_len < 1) return PMQA_ERR_NULL;
+  const pmqa_status sizes = check_logits_sizes(batch, next_n, page_size, out_row_stride, num_heads,
+                                               head_dim, block_table_stride);
+  if (sizes != PMQA_OK) return sizes;
+  const LogitsPlan pl = plan_logits(batch, next_n, page_size, out_row_stride, num_heads,
+                                    block_table_stride);
+  const int jw = pl.sh.rows_per_wave;
+  int n;
+  if (pl.flat) {
+    n = snprintf(name, (size_t)name_len, "logits_flat_kernel<%d,%d>", num_heads, jw);
+  } else {
+    int waves = 0, ring = 0;
+    pmqa::persistent_geometry(num_heads, jw, &waves, &ring);
+    n = snprintf(name, (size_t)name_len, "logits_kernel<%d,%d,%d,%d>", num_heads, jw, waves, ring);
+  }
+  return n >= 0 && n < name_len ? PMQA_OK : PMQA_ERR_SHAPE;
+}
+
 }  // extern "C"
 
 namespace {
@@ -48,13 +109,9 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
                         int32_t page_size, int32_t next_n, float* out, int64_t out_row_stride,
                         int32_t batch, int32_t num_heads, int32_t head_dim,
                         int64_t block_table_stride, void* stream, const pmqa::LaunchTiming& tm) {
-  if (batch < 0 || next_n < 1 || out_row_stride < 1 || block_table_stride < 1)
-    return PMQA_ERR_SHAPE;
-  if (!valid_page_size(page_size)) return PMQA_ERR_SHAPE;
-  if (head_dim != pmqa::kHeadDim) return PMQA_ERR_UNSUPPORTED;
-  if (!(num_heads == 16 || num_heads == 32 || num_heads == 64 || num_heads == 128))
-    return PMQA_ERR_UNSUPPORTED;
-  if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
+  const pmqa_status sizes = check_logits_sizes(batch, next_n, page_size, out_row_stride, num_heads,
+                                               head_dim, block_table_stride);
+  if (sizes != PMQA_OK) return sizes;
   if (batch == 0) return PMQA_OK;
   if (!q || !kv_cache || !weights || !context_lens || !block_tables || !out)
     return PMQA_ERR_NULL;
@@ -76,26 +133,23 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
   p.next_n = next_n;
   p.page_size = page_size;
   p.log2_page = log2_exact(page_size);
-  // the grid covers every token a request could have: the table row's capacity
-  // and the output row's width bound it
-  int64_t max_tokens = block_table_stride * (int64_t)page_size;
-  if (out_row_stride < max_tokens) max_tokens = out_row_stride;
-  if (max_tokens > INT32_MAX) max_tokens = INT32_MAX;
-  p.max_tokens = (int32_t)max_tokens;
-  const pmqa::LogitsShape sh = pmqa::logits_shape(num_heads, next_n);
-  const int64_t n_rgroups = (next_n + sh.rows_per_wave - 1) / sh.rows_per_wave;
+  const LogitsPlan pl = plan_logits(batch, next_n, page_size, out_row_stride, num_heads,
+                                    block_table_stride);
+  p.max_tokens = (int32_t)pl.max_tokens;
+  const pmqa::LogitsShape& sh = pl.sh;
+  const int64_t n_rgroups = pl.n_rgroups;
   // the grid's work units: enough to fill the chip, and at least 4 per request
   // so that the device-side split (runs never cross requests) stays balanced
   // when requests are long and few units are resident at once; never more
   // than the iterations the contexts could hold, never fewer than the batch
-  const int64_t max_iters = (int64_t)batch * ((max_tokens + sh.iter_tokens - 1) / sh.iter_tokens);
+  const int64_t max_iters = pl.max_iters;
   int64_t n_slices = sh.target_waves / n_rgroups;
   if (n_slices < 4 * (int64_t)batch) n_slices = 4 * (int64_t)batch;
   if (n_slices > max_iters) n_slices = max_iters;
   if (n_slices > INT32_MAX / n_rgroups) n_slices = INT32_MAX / n_rgroups;  // still >= batch
   p.n_slices = (int32_t)n_slices;
   p.n_rgroups = (int32_t)n_rgroups;
-  p.flat_items = n_rgroups == 1 && max_iters <= sh.flat_max_items ? max_iters : 0;
+  p.flat_items = pl.flat ? max_iters : 0;
   // small block tables and q rows are pulled into L2 at kernel start, while
   // the context lengths are read, so that the page-id and q loads that depend
   // on them hit L2

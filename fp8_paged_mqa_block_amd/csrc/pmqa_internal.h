@@ -48,6 +48,8 @@ struct LogitsShape {
                       // the possible iterations are at most this many (0: never)
 };
 LogitsShape logits_shape(int heads, int next_n);
+// Workgroup waves and iterations in flight of the persistent geometry.
+void persistent_geometry(int heads, int rows_per_wave, int* waves, int* ring);
 hipError_t launch_logits(const LogitsParams& p, const LogitsShape& sh, int heads,
                          const LaunchTiming& tm, hipStream_t stream);
 

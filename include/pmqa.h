@@ -241,6 +241,20 @@ PMQA_API const char* pmqa_status_string(pmqa_status status);
 /* Library version, as major*10000 + minor*100 + patch. */
 PMQA_API int32_t pmqa_version(void);
 
+/* Name of the logits kernel paged_mqa_logits launches for these sizes (host
+ * only: no GPU, no device memory), written NUL-terminated into name[0..name_len):
+ * "logits_flat_kernel<H,R>" (one single-wave workgroup per 64-token iteration,
+ * taken when every next_n row of a request fits one wave of 64 q rows and the
+ * iterations the contexts could hold are at most 8192) or
+ * "logits_kernel<H,R,W,D>" (the persistent grid: R next_n rows per wave, W waves
+ * per workgroup, D iterations in flight per wave).  The sizes are those of
+ * paged_mqa_logits and are checked the same way.  Returns PMQA_ERR_NULL for a
+ * NULL name or name_len < 1, and PMQA_ERR_SHAPE when the name does not fit. */
+PMQA_API pmqa_status pmqa_logits_kernel(int32_t batch, int32_t next_n, int32_t page_size,
+                                        int64_t out_row_stride, int32_t num_heads,
+                                        int32_t head_dim, int64_t block_table_stride,
+                                        char* name, int32_t name_len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -139,3 +139,32 @@ def test_quantize_k_cache_binding_rejects_wrong_dtypes():
     k = torch.zeros(4, 128, dtype=torch.float16)
     with pytest.raises(ValueError):
         pm.quantize_k_cache(k, torch.zeros(4, dtype=torch.int64), torch.zeros(1320, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("sizes, name", [
+    # the five workloads' shapes: (batch, next_n, page_size, out_row_stride, heads, table width)
+    ((2, 1, 64, 1024, 64, 16), "logits_flat_kernel<64,1>"),
+    ((64, 1, 64, 8192, 64, 128), "logits_flat_kernel<64,1>"),
+    ((256, 4, 256, 1 << 20, 128, 128), "logits_kernel<128,1,8,2>"),
+    ((128, 3, 8, 65536, 64, 8192), "logits_kernel<64,3,8,2>"),
+    ((32, 2, 64, 131072, 128, 2048), "logits_kernel<128,1,8,2>"),
+    # the single-wave geometry's bound: at most 8192 possible 64-token iterations
+    ((64, 1, 64, 8256, 64, 129), "logits_kernel<64,1,9,1>"),
+    ((128, 1, 64, 4096, 64, 64), "logits_flat_kernel<64,1>"),
+    ((16, 4, 16, 2048, 16, 128), "logits_flat_kernel<16,4>"),
+    ((16, 3, 16, 2048, 32, 128), "logits_kernel<32,3,4,4>"),
+])
+def test_logits_kernel_names(lib, sizes, name):
+    """The launch geometry paged_mqa_logits takes for given sizes (host only)."""
+    batch, next_n, ps, stride, heads, width = sizes
+    assert pm.logits_kernel(batch, next_n, ps, stride, heads, width) == name
+
+
+def test_logits_kernel_name_errors(lib):
+    buf = ctypes.create_string_buffer(8)
+    assert lib.pmqa_logits_kernel(2, 1, 64, 1024, 64, 128, 16, None, 8) == ERR_NULL
+    # the name does not fit
+    assert lib.pmqa_logits_kernel(2, 1, 64, 1024, 64, 128, 16, buf, len(buf)) == ERR_SHAPE
+    big = ctypes.create_string_buffer(64)
+    assert lib.pmqa_logits_kernel(2, 1, 64, 1024, 96, 128, 16, big, 64) == ERR_UNSUPPORTED
+    assert lib.pmqa_logits_kernel(2, 1, 48, 1024, 64, 128, 16, big, 64) == ERR_SHAPE
