@@ -753,8 +753,14 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
   const uint32_t nwg = gridDim.x;  // a multiple of 8
   const uint32_t wg = (blockIdx.x & 7u) * (nwg >> 3) + (blockIdx.x >> 3);
   // units are dealt wave-major over the workgroups, so that when fewer units
-  // than waves have work every CU still gets its share
-  const uint32_t wave = (uint32_t)wl * nwg + wg;
+  // than waves have work every CU still gets its share.  When the row groups
+  // of a unit fit a workgroup evenly, they take consecutive waves of one
+  // workgroup: they gather the same pages, which that CU's L1 may then serve
+  // once for all of them.
+  const uint32_t rg = (uint32_t)p.n_rgroups;
+  const uint32_t wave = (uint32_t)WAVES % rg == 0u
+                            ? ((uint32_t)wl / rg) * (nwg * rg) + wg * rg + (uint32_t)wl % rg
+                            : (uint32_t)wl * nwg + wg;
   const int unit = (int)(wave / (uint32_t)p.n_rgroups);
   const int j0 = (int)(wave % (uint32_t)p.n_rgroups) * JW;
 
