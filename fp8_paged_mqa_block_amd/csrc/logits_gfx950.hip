@@ -849,6 +849,76 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
   }
 }
 
+// One unit per workgroup, its next_n rows one per wave (G waves), sharing one
+// ring of RING K slots: every page is gathered once for all rows.  Wave w
+// issues the page ids and the gather of the iterations k with k % G == w; a
+// workgroup barrier per iteration publishes slot k (its owner waited for it
+// first) and frees slot k - 1 (every wave read it before the barrier) for the
+// gather of k + RING - 1.  Page ids of iteration k + L are issued just before
+// the gather of k, so the owner's wait for gather k proves them landed before
+// their own gather is issued (L >= RING - 1).  Every wave of a workgroup runs
+// the same run, hence the same number of barriers.
+template <int H, int G, int RING>
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void logits_shared_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t max_tokens,
+                          LogitsParams p) {
+  constexpr int L = ((RING - 1 + G - 1) / G) * G;
+  constexpr int NS = L / G + 1;
+  static_assert(RING % G == 0 && L >= RING - 1, "shared ring layout");
+  const CtxArgs ca{ctx_lens, batch, max_tokens};
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RING][kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t ids[G][NS][kMaxPages];
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15;
+  const int kq = lane >> 4;
+  const int wl = uniform(threadIdx.x >> 6);
+  const uint32_t nwg = gridDim.x;  // a multiple of 8
+  const int unit = (int)((blockIdx.x & 7u) * (nwg >> 3) + (blockIdx.x >> 3));
+  uint32_t* my_ids = &ids[wl][0][0];
+  auto id_slot = [&](int k) { return my_ids + ((k / G) % NS) * kMaxPages; };
+  {
+    const int64_t tline = ((int64_t)(blockIdx.x >> 3) * G + wl) * 64 + lane;
+    if (tline < p.warm_table_lines)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(p.tables) + tline * 128,
+                                       LDS_PTR(my_ids), 4, 0, 0);
+    const int64_t qline = ((int64_t)blockIdx.x * G + wl) * 64 + lane;
+    if (qline < p.warm_q_lines)
+      __builtin_amdgcn_global_load_lds(p.q + qline * 128, LDS_PTR(my_ids), 4, 0, 0);
+  }
+  Run run;
+  if (unit >= p.n_slices || !find_run(ca, p, unit, lane, run)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+  const int n_it = run.n_it;
+  const ChunkOffsets co = chunk_offsets(lane);
+  for (int k = wl; k < L; k += G)
+    if (k < n_it) issue_ids(p, run, run.it0 + k, lane, id_slot(k));
+  QRegs<H, 1> qr;
+  load_q<H, 1>(p, run.b, wl, m, kq, qr);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int k = wl; k < RING - 1; k += G) {
+    if (k >= n_it) break;
+    if (k + L < n_it) issue_ids(p, run, run.it0 + k + L, lane, id_slot(k + L));
+    issue_gather(p, run.it0 + k, run.ctx_eff, id_slot(k), lane, co, &ring[k % RING][0]);
+  }
+  for (int k = 0; k < n_it; ++k) {
+    if (k % G == wl) {
+      // own gathers issued after k's: k + G, k + 2G, ... up to k + RING - 2
+      const int last = min(k + RING - 2, n_it - 1);
+      wait_vm(kGatherLoads * (last > k ? (last - k) / G : 0));
+    }
+    __builtin_amdgcn_s_barrier();
+    const int nx = k + RING - 1;
+    if (nx < n_it && nx % G == wl) {
+      if (nx + L < n_it) issue_ids(p, run, run.it0 + nx + L, lane, id_slot(nx + L));
+      issue_gather(p, run.it0 + nx, run.ctx_eff, id_slot(nx), lane, co, &ring[nx % RING][0]);
+    }
+    score<H, 1>(p, run, run.it0 + k, wl, lane, qr, &ring[k % RING][0]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
 // Flat geometry for small units (all next_n rows of a request within 64 q
 // rows): a work item is one 64-token iteration of one request, and every wave
 // is a workgroup of its own.  The grid is at most one residency of the chip
@@ -1100,6 +1170,21 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
       else
         hipLaunchKernelGGL(kern, dim3(n_wg), dim3(64), 0, stream, p.ctx, p.batch, p.max_tokens,
                            p.tables, warm, p.q, warm_q, p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (H == 128 && JW == 1) {
+    const int ring = shared_ring_depth(H, JW, p.n_rgroups);
+    if (ring > 0) {
+      // one unit per workgroup of n_rgroups waves
+      const uint32_t n_wg = ((uint32_t)p.n_slices + 7u) & ~7u;
+      auto kern = ring == 8 ? logits_shared_kernel<128, 4, 8> : logits_shared_kernel<128, 2, 4>;
+      const dim3 block(64 * p.n_rgroups);
+      if (tm.start || tm.stop)
+        hipExtLaunchKernelGGL(kern, dim3(n_wg), block, 0, stream, tm.start, tm.stop, 0, p.ctx,
+                              p.batch, p.max_tokens, p);
+      else
+        hipLaunchKernelGGL(kern, dim3(n_wg), block, 0, stream, p.ctx, p.batch, p.max_tokens, p);
       return hipGetLastError();
     }
   }

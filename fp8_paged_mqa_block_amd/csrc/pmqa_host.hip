@@ -92,6 +92,9 @@ pmqa_status pmqa_logits_kernel(int32_t batch, int32_t next_n, int32_t page_size,
   int n;
   if (pl.flat) {
     n = snprintf(name, (size_t)name_len, "logits_flat_kernel<%d,%d>", num_heads, jw);
+  } else if (const int sring = pmqa::shared_ring_depth(num_heads, jw, (int)pl.n_rgroups)) {
+    n = snprintf(name, (size_t)name_len, "logits_shared_kernel<%d,%d,%d>", num_heads,
+                 (int)pl.n_rgroups, sring);
   } else {
     int waves = 0, ring = 0;
     pmqa::persistent_geometry(num_heads, jw, &waves, &ring);

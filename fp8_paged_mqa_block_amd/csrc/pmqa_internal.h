@@ -48,6 +48,12 @@ struct LogitsShape {
                       // the possible iterations are at most this many (0: never)
 };
 LogitsShape logits_shape(int heads, int next_n);
+// Ring depth of the shared-ring geometry, or 0 where it does not apply: one
+// next_n row per wave of 128 heads, with 2 or 4 rows per request (a
+// workgroup of 4 or 2 waves' units then holds 8 or 4 slots).
+inline constexpr int shared_ring_depth(int heads, int rows_per_wave, int n_rgroups) {
+  return heads == 128 && rows_per_wave == 1 ? (n_rgroups == 4 ? 8 : (n_rgroups == 2 ? 4 : 0)) : 0;
+}
 // Workgroup waves and iterations in flight of the persistent geometry.
 void persistent_geometry(int heads, int rows_per_wave, int* waves, int* ring);
 hipError_t launch_logits(const LogitsParams& p, const LogitsShape& sh, int heads,

@@ -145,14 +145,16 @@ def test_quantize_k_cache_binding_rejects_wrong_dtypes():
     # the five workloads' shapes: (batch, next_n, page_size, out_row_stride, heads, table width)
     ((2, 1, 64, 1024, 64, 16), "logits_flat_kernel<64,1>"),
     ((64, 1, 64, 8192, 64, 128), "logits_flat_kernel<64,1>"),
-    ((256, 4, 256, 1 << 20, 128, 128), "logits_kernel<128,1,8,2>"),
+    ((256, 4, 256, 1 << 20, 128, 128), "logits_shared_kernel<128,4,8>"),
     ((128, 3, 8, 65536, 64, 8192), "logits_kernel<64,3,8,2>"),
-    ((32, 2, 64, 131072, 128, 2048), "logits_kernel<128,1,8,2>"),
+    ((32, 2, 64, 131072, 128, 2048), "logits_shared_kernel<128,2,4>"),
     # the single-wave geometry's bound: at most 8192 possible 64-token iterations
     ((64, 1, 64, 8256, 64, 129), "logits_kernel<64,1,9,1>"),
     ((128, 1, 64, 4096, 64, 64), "logits_flat_kernel<64,1>"),
     ((16, 4, 16, 2048, 16, 128), "logits_flat_kernel<16,4>"),
     ((16, 3, 16, 2048, 32, 128), "logits_kernel<32,3,4,4>"),
+    # 128 heads: next_n 3 keeps one ring per wave, 1 row per request the flat geometry
+    ((8, 3, 64, 4096, 128, 64), "logits_kernel<128,1,8,2>"),
 ])
 def test_logits_kernel_names(lib, sizes, name):
     """The launch geometry paged_mqa_logits takes for given sizes (host only)."""

@@ -40,6 +40,10 @@ SMALL = [
     dict(batch=4, next_n=2, heads=64, page_size=128, ctx_range=(100, 1100)),
     dict(batch=3, next_n=5, heads=64, page_size=64, ctx_range=(0, 400)),
     dict(batch=3, next_n=3, heads=128, page_size=8, ctx_range=(1, 300)),
+    # 128 heads with 4 rows per request: one shared K ring per request, runs
+    # shorter and longer than its 8 slots, small pages and empty contexts
+    dict(batch=6, next_n=4, heads=128, page_size=8, ctx_range=(0, 700), zero_every=3),
+    dict(batch=4, next_n=4, heads=128, page_size=64, context_lens=[1, 64, 450, 1100]),
     dict(batch=4, next_n=4, heads=16, page_size=256, ctx_range=(0, 800)),
     dict(batch=2, next_n=1, heads=64, page_size=16,
          context_lens=[1, 15]),
@@ -317,6 +321,7 @@ def test_topk_special_rows(gpu_lib):
     dict(batch=64, next_n=2, heads=32, page_size=8),   # single-wave geometry, small pages
     dict(batch=5, next_n=3, heads=64, page_size=8),    # persistent geometry, 192-row units
     dict(batch=3, next_n=1, heads=128, page_size=256),  # persistent geometry, 128-row units
+    dict(batch=3, next_n=4, heads=128, page_size=64),  # shared-ring geometry
 ])
 def test_all_contexts_empty(gpu_lib, shape):
     """A batch whose every context is empty: nothing is scored, every output
