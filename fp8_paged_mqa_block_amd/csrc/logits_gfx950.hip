@@ -562,15 +562,22 @@ __device__ __forceinline__ void wait_vm(int n) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Sum of the value held by lanes l, l^16, l^32 and l^48 (the four 16-lane rows
-// of the wave), on every lane: two row swaps, no LDS traffic.
-__device__ __forceinline__ float sum_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+// Reduce-scatter of four per-tile partial sums over the four 16-lane rows of
+// the wave: lane l of row r returns the sum, over the rows, of tile r's value
+// at lanes l % 16 + 16 * r' (r' = 0..3), added as (rows 0 + 2) + (rows 1 + 3).
+// The half swap pairs tiles 0/2 and 1/3 (lanes 0-31 keep the first tile's
+// pair sums, lanes 32-63 the second's); the row swap then pairs the two.
+// Three swaps and three adds for the four tiles.
+__device__ __forceinline__ float reduce_tiles(float p0, float p1, float p2, float p3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false,
                                                   false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false,
+  const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false,
                                                   false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const float s13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // max(x, 0) on the bit pattern: positive floats are positive as int32, and
@@ -596,9 +603,8 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
   constexpr int HT = H / 16;
   const int kq = lane >> 4;
   const int t0 = it * kIterTokens;
-  float keep[JW];
-#pragma unroll
-  for (int jj = 0; jj < JW; ++jj) keep[jj] = 0.f;
+  static_assert(kTilesPerIter == 4, "reduce_tiles takes four tiles");
+  float part[JW][kTilesPerIter];
 #pragma unroll
   for (int tile = 0; tile < kTilesPerIter; ++tile) {
     const float s = sc[tile];
@@ -621,10 +627,25 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
             sum = __builtin_fmaf(qr.wv[jj][ht][i], __builtin_fmaxf(acc[ht][i] * s, 0.f), sum);
         }
       }
-      sum = sum_rows(sum);
-      if constexpr (FACTORED) sum *= s;
-      if (kq == tile) keep[jj] = sum;
+      part[jj][tile] = sum;
     }
+  }
+  // this lane's row kq ends with tile kq's tokens: its scale multiplies the
+  // head-weighted sum in the factored form
+  // (the scales pass through an empty asm statement as plain values: a
+  // select among elements of sc would become an indexed load, which puts the
+  // operands in scratch memory)
+  float s0 = sc[0], s1 = sc[1], s2 = sc[2], s3 = sc[3];
+  asm volatile("" : "+v"(s0), "+v"(s1), "+v"(s2), "+v"(s3));
+  float s_own = s0;
+  s_own = kq == 1 ? s1 : s_own;
+  s_own = kq == 2 ? s2 : s_own;
+  s_own = kq == 3 ? s3 : s_own;
+  float keep[JW];
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) {
+    keep[jj] = reduce_tiles(part[jj][0], part[jj][1], part[jj][2], part[jj][3]);
+    if constexpr (FACTORED) keep[jj] *= s_own;
   }
   const float neg_inf = -__builtin_inff();
   const int t = t0 + lane;
