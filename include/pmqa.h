@@ -245,7 +245,9 @@ PMQA_API int32_t pmqa_version(void);
  * only: no GPU, no device memory), written NUL-terminated into name[0..name_len):
  * "logits_flat_kernel<H,R>" (one single-wave workgroup per 64-token iteration,
  * taken when every next_n row of a request fits one wave of 64 q rows and the
- * iterations the contexts could hold are at most 8192) or
+ * iterations the contexts could hold are at most 8192),
+ * "logits_shared_kernel<H,G,D>" (128 heads with 2 or 4 next_n rows: one request
+ * run per workgroup of G waves, one row each, around one ring of D K slots) or
  * "logits_kernel<H,R,W,D>" (the persistent grid: R next_n rows per wave, W waves
  * per workgroup, D iterations in flight per wave).  The sizes are those of
  * paged_mqa_logits and are checked the same way.  Returns PMQA_ERR_NULL for a
