@@ -344,13 +344,23 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     uint32_t off_a = run_a + lane_of(pa, wave) - ca;  // exclusive over waves
     uint32_t off_e = run_e + lane_of(pe, wave) - ce;
     const int64_t base = (int64_t)c * kChunk + thread_base;
+    // the flags pass through an empty asm statement so that the ballots below
+    // are taken again instead of keeping the first loop's 2 * KPT masks live
+    // in scalar registers across the barrier
+    int fa[KPT], fe[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const uint64_t ma = __ballot(is_a[j]);
-      const uint64_t me = __ballot(is_e[j]);
+      fa[j] = is_a[j];
+      fe[j] = is_e[j];
+      asm volatile("" : "+v"(fa[j]), "+v"(fe[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t ma = __ballot(fa[j] != 0);
+      const uint64_t me = __ballot(fe[j] != 0);
       const int32_t idx = (int32_t)(base + 64 * j);
-      if (is_a[j]) out[off_a + (uint32_t)lane_rank(ma)] = idx;
-      if (is_e[j]) {
+      if (fa[j]) out[off_a + (uint32_t)lane_rank(ma)] = idx;
+      if (fe[j]) {
         const uint32_t rank = off_e + (uint32_t)lane_rank(me);
         if (rank_bin) {
           sh.cand_key[rank] = cc.key[j];
