@@ -29,9 +29,9 @@ def visible_len(ctx: int, next_n: int, j: int) -> int:
 
     Reading adopted for the causal mask: the ``next_n`` query rows of a request
     are the last ``next_n`` positions of its context, so position ``j`` sees
-    tokens ``t <= ctx - next_n + j``.  Clamped to ``[0, ctx]``, which gives the
-    empty-context MTP case of aiter PR #6626 ("Accuracy": decode, and MTP with
-    next_n=3 and an empty context) no visible token.  For next_n = 1 every row
+    tokens ``t <= ctx - next_n + j``.  Clamped to ``[0, ctx]``, so a request
+    with an empty context (aiter PR #6626, "Accuracy", tests one under MTP with
+    three positions) gives its rows no visible token.  For next_n = 1 every row
     sees its whole context.
     """
     v = int(ctx) - int(next_n) + int(j) + 1

@@ -60,4 +60,5 @@ def assemble(ex):
 
 
 def expected_value(v):
-    return float("-inf") if v == "-inf" else float(v)
+    """A golden value: a number, or the strings "-inf" / "nan"."""
+    return float(v)

@@ -11,7 +11,11 @@ Each is exact (bit-identical) in the oracle:
 * row coverage of a [1024, 1<<20] fp32 output, with a negative control that
   plants a 32-bit byte-offset store in the oracle and must reproduce the first
   untouched rows the page prints (512 at 1<<20 columns, 895 at 600000);
-* int64 page ids: a page whose byte offset passes 2^31 is read correctly.
+* int64 page ids: a page whose byte offset passes 2^31 is read correctly, with
+  a negative control that plants an int32 id * record-size product in the
+  oracle's gather and must reproduce the wrap boundary ATOM PR #2533 prints
+  (row 3,728,270 of 576-byte records, block 233,016 of 16) and this path's own
+  (page 2,033,602 of 8-token pages).
 """
 import math
 
@@ -240,3 +244,83 @@ def test_int64_page_ids_past_2gib():
     rows = oracle.paged_mqa_logits(q, pool, np.ones((1, 1), np.float32),
                                    np.array([1], np.int32), np.array([[hi_page]], np.int64), ps, 1)
     assert rows[0].tolist() == [5.0]  # (1+2+3+4) * 0.5
+
+
+def _offset_int32(row_id, row_bytes):
+    """The byte offset row_id * row_bytes as a product in int32 arithmetic
+    (two's complement wrap), the failure ATOM PR #2533 describes."""
+    v = (int(row_id) * int(row_bytes)) & 0xFFFFFFFF
+    return v - (1 << 32) if v >= 1 << 31 else v
+
+
+def _gather_int32(kv_cache, table_row, ctx, page_size, head_dim):
+    """The oracle's gather with the planted mistake: each record's byte offset is
+    the int32 product of its cache row id and the record size.  A wrapped
+    (negative) offset lands outside the pool: its values read back as NaN."""
+    rec = head_dim + 4
+    flat = kv_cache.reshape(-1)
+    k = np.full((ctx, head_dim), np.nan)
+    scale = np.full(ctx, np.nan)
+    for t in range(ctx):
+        row = int(table_row[t // page_size]) * page_size + t % page_size
+        off = _offset_int32(row, rec)
+        if 0 <= off and off + rec <= flat.size:
+            k[t] = oracle.e4m3fn_to_float64(flat[off:off + head_dim])
+            scale[t] = float(np.frombuffer(flat[off + head_dim:off + rec].tobytes(), "<f4")[0])
+    return k, scale
+
+
+def test_int32_row_ids_wrap_where_the_page_says(monkeypatch):
+    """Negative control for int64 ids.  ATOM PR #2533 (description) reports that a
+    token-level table of int32 ids multiplied by the 576-byte MLA row stride
+    wraps for rows past 2**31 / 576 = 3,728,270, i.e. from block 233,016 of 16
+    tokens.  Planting that int32 product in the oracle's gather reproduces the
+    boundary exactly: the last row below it is read correctly, the first row
+    past it is not, while the real (int64) oracle reads both.  The same planted
+    gather on this path's own records (132 bytes, 8-token pages) goes wrong
+    from page ceil(2^31 / 1056) = 2,033,602, the boundary the small-pages
+    workload's pool is sized to cross."""
+    assert 2 ** 31 // 576 == 3_728_270
+    first_bad = next(r for r in range(3_728_260, 3_728_280) if _offset_int32(r, 576) < 0)
+    assert first_bad == 3_728_270 + 1 and first_bad // 16 == 233_016
+    assert _offset_int32(3_728_270, 576) == 3_728_270 * 576
+
+    # MLA-sized records (572 codes + the fp32 scale = 576 bytes), token-level
+    # table, a pool past the boundary (lazily backed zeros)
+    from tests.handcase import codes_of
+    D, rows_in_pool = 572, first_bad + 2
+    pool = np.zeros(rows_in_pool * (D + 4), dtype=np.uint8)
+    ids = [first_bad - 1, first_bad]
+    for i, r in enumerate(ids):
+        off = r * (D + 4)
+        pool[off:off + D] = codes_of([float(i + 1)] * D)
+        pool[off + D:off + D + 4] = np.frombuffer(np.float32(1.0).tobytes(), np.uint8)
+    q = codes_of([1.0] * D).reshape(1, 1, D)
+    args = (q, pool, np.ones((1, 1), np.float32), np.array([2], np.int32),
+            np.array([ids], np.int64), 1, 1)
+    good = oracle.paged_mqa_logits(*args)[0]
+    assert good.tolist() == [572.0, 1144.0]
+    monkeypatch.setattr(opm, "gather_request", _gather_int32)
+    bad = oracle.paged_mqa_logits(*args)[0]
+    assert bad[0] == 572.0 and np.isnan(bad[1])
+    monkeypatch.undo()
+
+    # this path's records: 8-token pages of 132-byte records
+    ps, D = 8, 128
+    page_bytes = ps * (D + 4)
+    boundary = -(-(2 ** 31) // page_bytes)
+    assert boundary == 2_033_602
+    assert _offset_int32(boundary * ps, D + 4) < 0 <= _offset_int32(boundary * ps - 1, D + 4)
+    pool = np.zeros((boundary + 1) * page_bytes, dtype=np.uint8)
+    for i, pg in enumerate((boundary - 1, boundary)):
+        off = pg * page_bytes
+        pool[off:off + D] = codes_of([float(i + 1)] * D)
+        pool[off + D:off + D + 4] = np.frombuffer(np.float32(0.5).tobytes(), np.uint8)
+    q = codes_of([1.0] * D).reshape(1, 1, D)
+    args = (q, pool, np.ones((1, 1), np.float32), np.array([9], np.int32),
+            np.array([[boundary - 1, boundary]], np.int64), ps, 1)
+    good = oracle.paged_mqa_logits(*args)[0]
+    assert good[0] == 64.0 and good[8] == 128.0
+    monkeypatch.setattr(opm, "gather_request", _gather_int32)
+    bad = oracle.paged_mqa_logits(*args)[0]
+    assert bad[0] == 64.0 and np.isnan(bad[8])

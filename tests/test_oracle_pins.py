@@ -112,13 +112,46 @@ def test_full_score_close_to_fractions(seed):
     H, D, n = 4, 16, 6
     qc = _finite_codes(rng, (1, H, D))
     kc = _finite_codes(rng, (n, D))
-    s = rng.random(n).astype(np.float32) * 3
+    # scales of both signs: relu acts on scale * dot, so a negative scale
+    # selects the heads whose dot is negative
+    s = ((rng.random(n) - 0.5) * 6).astype(np.float32)
     w = rng.standard_normal((1, H)).astype(np.float32)
     rows = oracle.request_logits(qc, w, oracle.e4m3fn_to_float64(kc), s.astype(np.float64), 1)
     for t in range(n):
         exact = _frac_logit(qc[0], kc[t], s[t], w[0])
-        mag = sum(abs(Fraction(float(w[0, h]))) for h in range(H)) * 448 * 448 * D * Fraction(float(s[t]))
+        mag = sum(abs(Fraction(float(w[0, h]))) for h in range(H)) * 448 * 448 * D * abs(Fraction(float(s[t])))
         assert abs(Fraction(float(rows[0][t])) - exact) <= mag * Fraction(1, 2 ** 50)
+
+
+def test_negative_scale_golden_rejects_a_factored_relu(monkeypatch):
+    """Plant s * relu(dot) (right only for s >= 0) in the oracle: the hand-derived
+    negative-scale example must then fail, so the golden pins the order of scale
+    and relu."""
+    import oracle.paged_mqa as opm
+
+    ex = [e for e in load_golden("worked_examples.json")["examples"]
+          if e["name"].startswith("E5_")][0]
+    a = assemble(ex)
+
+    def factored(q_req, w_req, k, scale, next_n):
+        q = oracle.e4m3fn_to_float64(q_req)
+        w = np.asarray(w_req, dtype=np.float64)
+        out = []
+        for j in range(next_n):
+            vis = oracle.visible_len(k.shape[0], next_n, j)
+            act = np.maximum(q[j] @ k[:vis].T, 0.0) * scale[None, :vis]
+            out.append(w[j] @ act)
+        return out
+
+    want = [expected_value(v) for v in ex["expected_rows"][0]]
+    rows = oracle.paged_mqa_logits(a["q"], a["kv_cache"], a["weights"], a["context_lens"],
+                                   a["block_tables"], a["page_size"], 1)
+    assert rows[0].tolist() == want
+    monkeypatch.setattr(opm, "request_logits", factored)
+    planted = oracle.paged_mqa_logits(a["q"], a["kv_cache"], a["weights"], a["context_lens"],
+                                      a["block_tables"], a["page_size"], 1)
+    assert planted[0].tolist() != want
+    assert planted[0].tolist() == [-0.25, 0.5, 0.0]
 
 
 # ---------------------------------------------------------------- worked examples
@@ -141,7 +174,7 @@ def test_worked_examples(ex):
         ctx = ex["requests"][r // nn]["ctx"]
         assert len(exp) == ctx
         got = out2[r, :ctx].astype(np.float64)
-        assert np.array_equal(got, np.asarray(exp)), (r, got, exp)
+        assert np.array_equal(got, np.asarray(exp), equal_nan=True), (r, got, exp)
         assert np.all(out2[r, ctx:] == sentinel)
         if "expected_visible" in ex:
             assert len(rows[r]) == ex["expected_visible"][r]
