@@ -160,6 +160,9 @@ def paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Ten
     _need(out.dim() == 2 and out.shape[0] == B * next_n and out.is_contiguous(),
           "out must be a contiguous [B*next_n, cols] tensor")
     ts = block_tables.shape[1]
+    # a [B, 0] table cannot hold any page: the stride it would pass (1) would
+    # let the kernel read an entry the tensor does not have
+    _need(ts >= 1 or B == 0, "block_tables must have at least one entry per request")
     st = lib.paged_mqa_logits(q.data_ptr(), kv_cache.data_ptr(), weights.data_ptr(),
                               context_lens.data_ptr(), block_tables.data_ptr(), int(page_size),
                               int(next_n), out.data_ptr(), int(out.shape[1]), int(B), H, D,
@@ -231,6 +234,7 @@ def check_inputs(context_lens: torch.Tensor, block_tables: torch.Tensor, page_si
     B = context_lens.shape[0]
     _need(block_tables.dtype == torch.int64 and block_tables.dim() == 2 and block_tables.shape[0] == B
           and block_tables.is_contiguous(), "block_tables must be a contiguous [B, W] int64 tensor")
+    _need(block_tables.shape[1] >= 1 or B == 0, "block_tables must have at least one entry per request")
     result = torch.empty(2, dtype=torch.int32, device=context_lens.device)
     st = lib.pmqa_check_inputs(context_lens.data_ptr(), block_tables.data_ptr(), int(B), int(page_size),
                                int(max(block_tables.shape[1], 1)), int(out_row_stride), int(num_pages),

@@ -480,8 +480,9 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
 //    and never used; a placeholder gather (`limit` 0, only keeping the
 //    instruction count fixed) reads the pool's first 64 records.
 //  * Smaller pages: each chunk takes its record's page id; chunks of records
-//    at or past `limit` fetch from the pool's first KiB instead and never use
-//    their page id.
+//    at or past `limit` fetch a chunk of the pool's first record instead (one
+//    cache line, inside any pool that holds a record) and never use their
+//    page id.
 __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int limit,
                                              const uint32_t* ids_slot, int lane,
                                              const ChunkOffsets& co, uint8_t* slot) {
@@ -523,7 +524,7 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
 #pragma unroll
   for (int i = 0; i < kGatherLoads; ++i) {
     const int64_t off = t0 + (int)rec[i] < limit ? (int64_t)((uint64_t)pg.id[i] * pb + in_page[i])
-                                                 : (int64_t)(16 * lane);
+                                                 : (int64_t)(16 * (lane & 7));
     __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
   }
 }
@@ -590,11 +591,18 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// max(y, 0) that passes NaN through, whatever its sign bit: a NaN scale makes
+// the token's score NaN, as max with NaN propagation gives (the reading adopted
+// for a NaN scale), where the hardware max would return 0.  -0 stays -0, which
+// compares equal to 0.
+__device__ __forceinline__ float relu_nan(float y) { return y < 0.f ? 0.f : y; }
+
 // Score one iteration (64 tokens x the wave's rows) from its slot operands and
 // store it.  FACTORED: every scale of the iteration is >= 0, so
 // relu(s * x) = s * relu(x) and the scale multiplies the head-weighted sum once
 // per token instead of once per head (2 VALU operations per MFMA output
-// instead of 3); otherwise the literal form runs.
+// instead of 3); otherwise the literal form runs (relu of scale * dot per head,
+// a NaN scale giving a NaN score).
 template <int H, int JW, bool EXACT, bool FACTORED>
 __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run& c, int it, int j0,
                                                 int lane, const QRegs<H, JW>& qr,
@@ -624,7 +632,7 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
           if constexpr (FACTORED)
             sum = __builtin_fmaf(qr.wv[jj][ht][i], relu_bits(acc[ht][i]), sum);
           else
-            sum = __builtin_fmaf(qr.wv[jj][ht][i], __builtin_fmaxf(acc[ht][i] * s, 0.f), sum);
+            sum = __builtin_fmaf(qr.wv[jj][ht][i], relu_nan(acc[ht][i] * s), sum);
         }
       }
       part[jj][tile] = sum;
@@ -728,7 +736,7 @@ __device__ __forceinline__ void score_ops(const LogitsParams& p, const Run& c, i
   for (int tile = 0; tile < kTilesPerIter; ++tile) {
     // tokens past the context: scale 0, never stored
     op.sc[tile] = t0 + tile * kTile < c.ctx_eff ? op.sc[tile] : 0.f;
-    bad |= !(op.sc[tile] >= 0.f);  // NaN also takes the literal form
+    bad |= !(op.sc[tile] >= 0.f);  // NaN takes the literal form, which passes it on
   }
   const bool factored = __ballot(bad) == 0;
   if (min_vis < kExactRows) {

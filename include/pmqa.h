@@ -19,7 +19,11 @@
  *     logit[r, t] = sum_h  w[r, h] * relu( scale_t * sum_d q[r, h, d] * k_t[d] )
  *
  * with q and k in OCP e4m3fn and the product accumulated in fp32 on the fp8
- * matrix cores.  Causal mask (reading adopted for MTP): the next_n rows of a
+ * matrix cores.  Scales may take either sign: relu acts on scale * dot, so a
+ * negative scale selects the heads whose dot is negative.  A NaN scale gives
+ * its token a NaN score in every row that sees it (relu passes NaN on) and
+ * changes nothing else.  Infinite scales, NaN codes and scores beyond the fp32
+ * range are outside the contract, as is the top-k order of NaN scores.  Causal mask (reading adopted for MTP): the next_n rows of a
  * request are its last next_n positions, so row j sees
  * visible = clamp(ctx_b - next_n + j + 1, 0, ctx_b) tokens; columns
  * [visible, ctx_b) receive -inf and columns >= ctx_b are never written.
@@ -70,8 +74,8 @@ typedef enum {
  *               4-byte aligned.  Token s of page p is the record starting at
  *               byte (p*page_size + s)*(head_dim+4): head_dim e4m3fn codes then
  *               the token's fp32 scale, little endian (the pages' cache is
- *               [num_blocks, block_size, 1, D+4] fp8 whose last 4 bytes per
- *               token are viewed as one fp32 scale).  Byte offsets are formed in
+ *               [num_blocks, block_size, 1, D+4] fp8, the trailing four bytes
+ *               of each token reinterpreted as its scale).  Byte offsets are formed in
  *               64-bit, so pools larger than 2^31 / 2^32 bytes are addressed
  *               correctly (ATOM PR #2533 "Address Triton decode KV rows with
  *               int64 ids").

@@ -138,8 +138,18 @@ def build_workload(
     ctx_fixups: Optional[dict] = None,
     zero_every: int = 0,
     padded_width: Optional[int] = None,
+    neg_scale_blocks: float = 0.0,
+    nan_scale_tokens: int = 0,
 ) -> Workload:
-    """Build one workload; see the module docstring for layout and draw order."""
+    """Build one workload; see the module docstring for layout and draw order.
+
+    ``neg_scale_blocks`` (a fraction) and ``nan_scale_tokens`` (a count per
+    request) perturb the stored scales after every other draw, so the rest of
+    the workload is unchanged: each 64-token block of a request is picked with
+    that probability, and inside a picked block every token's scale is negated
+    with probability 1/2 (blocks of mixed signs next to blocks of scales >= 0);
+    then that many distinct tokens per request get a NaN scale.  The codes are
+    untouched."""
     rng = np.random.default_rng(seed)
     D, H, ps, B = head_dim, heads, page_size, batch
     rec = D + 4
@@ -209,6 +219,23 @@ def build_workload(
         w = rng.random((B * next_n, H), dtype=np.float32)
     else:
         w = (rng.standard_normal((B * next_n, H), dtype=np.float32) / np.float32(math.sqrt(H))).astype(np.float32)
+
+    # 6. optional scale perturbations (sign flips, NaN), after every other draw
+    if neg_scale_blocks > 0.0 or nan_scale_tokens > 0:
+        for b in range(B):
+            n = int(ctx[b])
+            if n == 0:
+                continue
+            t = np.arange(n, dtype=np.int64)
+            rows = tables[b, t // ps] * ps + (t % ps)
+            sc = recs[rows, D:].copy().view("<f4").reshape(n)
+            if neg_scale_blocks > 0.0:
+                picked = rng.random((n + 63) // 64) < neg_scale_blocks
+                flip = picked[t // 64] & (rng.random(n) < 0.5)
+                sc = np.where(flip, -sc, sc).astype(np.float32)
+            if nan_scale_tokens > 0:
+                sc[rng.choice(n, min(n, nan_scale_tokens), replace=False)] = np.float32(np.nan)
+            recs[rows, D:] = sc.astype("<f4").view(np.uint8).reshape(n, 4)
 
     wl = Workload(
         name=name,

@@ -2,9 +2,9 @@
 
 Small cases are compared element by element on every row (several 16-token
 tiles, 64-token iterations and 256-token wave units, with ragged tails, every
-page size, head count and next_n class, zero contexts).  The five workloads run
-at full size in the launch configuration the benchmark times; their rows are
-checked on sampled requests (the oracle computes them one by one), plus
+page size, head count and next_n class, zero contexts, scales of both signs
+and NaN scales).  The five workloads run at full size in the launch
+configuration the benchmark times, every row compared with the oracle, plus
 properties that hold at any size: full-row coverage of the [1024, 1<<20]
 output, no write past a context, bit-identical results across compact and
 padded tables, output strides, batch splits, table permutations and repeat
@@ -158,15 +158,12 @@ def test_config3_wide_output_rows_past_2gib(gpu_lib, cfg3):
         assert bool((~untouched).any(dim=1).all()), f"untouched row in [{r0}, {r0 + 64})"
         past = cols[None, :] >= ctx_rows[r0 : r0 + 64, None]
         assert not bool((past & ~untouched).any()), f"write past a context in [{r0}, {r0 + 64})"
-    # sampled requests vs the oracle: both sides of the 2^31-byte boundary
-    rng = np.random.default_rng(0)
-    reqs = sorted(set([0, 127, 128, 255] + rng.choice(wl.batch, 4, replace=False).tolist()))
-    ref = oracle_rows(wl, requests=reqs)
-    worst = check_rows(wl, out, ref, requests=reqs)
-    say(f"config3 sampled worst rel err {worst:.3e}")
+    # every request vs the oracle (rows on both sides of the 2^31-byte boundary)
+    ref = oracle_rows(wl)
+    worst = check_rows(wl, out, ref)
+    say(f"config3 worst rel err {worst:.3e} over all {wl.rows} rows")
     idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
-    rows = [r for b in reqs for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
-    check_topk(idx, ref, wl.topk, rows=rows)
+    check_topk(idx, ref, wl.topk)
 
 
 @pytest.fixture(scope="module")
@@ -187,14 +184,14 @@ def test_config4_small_pages_compact_and_padded(gpu_lib, cfg4):
     high = [b for b in range(wl.batch) if (wl.block_tables[b, : npg[b]] >= boundary).any()]
     assert high
     zero = [b for b in range(wl.batch) if wl.context_lens[b] == 0]
-    reqs = sorted(set([1, 2, 3, 4, 5] + high[:3]) - set(zero))
-    ref = oracle_rows(wl, requests=reqs)
-    worst = check_rows(wl, out, ref, requests=reqs)
+    # every request vs the oracle, including those reading pages past 2^31 bytes
+    ref = oracle_rows(wl)
+    worst = check_rows(wl, out, ref)
     check_untouched_rows(wl, out, zero)
-    say(f"config4 sampled worst rel err {worst:.3e}")
+    say(f"config4 worst rel err {worst:.3e} over all {wl.rows} rows ({len(high)} requests "
+        f"read pages past 2^31 bytes)")
     idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
-    rows = [r for b in reqs for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
-    check_topk(idx, ref, wl.topk, rows=rows)
+    check_topk(idx, ref, wl.topk)
     zrows = [r for b in zero for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
     assert bool((idx[zrows] == -1).all())
 
@@ -234,13 +231,11 @@ def test_config5_long_context(gpu_lib):
     wl = synth.make_config(5)
     d = upload(wl)
     out = run_logits(gpu_lib, wl, d)
-    reqs = [0, 13, 31]
-    ref = oracle_rows(wl, requests=reqs)
-    worst = check_rows(wl, out, ref, requests=reqs)
-    say(f"config5 sampled worst rel err {worst:.3e}")
+    ref = oracle_rows(wl)
+    worst = check_rows(wl, out, ref)
+    say(f"config5 worst rel err {worst:.3e} over all {wl.rows} rows")
     idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
-    rows = [r for b in reqs for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
-    check_topk(idx, ref, wl.topk, rows=rows)
+    check_topk(idx, ref, wl.topk)
 
 
 @pytest.mark.parametrize("ties", [0, 3])
@@ -477,3 +472,133 @@ def test_randomized_small_workloads(gpu_lib):
         check_rows(wl, out, ref)
         idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
         check_topk(idx, ref, wl.topk)
+
+
+# One shape per logits kernel family (the flat single-wave grid, the persistent
+# grid at 64 and 128 heads, the shared K ring at 128 heads with 2 or 4 rows).
+FAMILIES = [
+    dict(heads=64, next_n=1, family="logits_flat_kernel"),
+    dict(heads=64, next_n=3, family="logits_kernel"),
+    dict(heads=128, next_n=1, family="logits_kernel"),
+    dict(heads=128, next_n=2, family="logits_shared_kernel"),
+    dict(heads=128, next_n=4, family="logits_shared_kernel"),
+]
+
+
+@pytest.mark.parametrize("page_size", [8, 64])
+@pytest.mark.parametrize("case", range(len(FAMILIES)))
+def test_signed_and_nan_scales(gpu_lib, case, page_size):
+    """Scales of both signs: 64-token blocks whose scales are all >= 0 sit next
+    to blocks with negated scales, so iterations take both the factored form
+    (s * relu(dot)) and the literal one (relu(s * dot)); rows shorter than 128
+    visible tokens (the exact-sum path) and longer ones.  Then NaN scales: the
+    rows that see such a token score NaN exactly there, as the oracle does."""
+    c = FAMILIES[case]
+    lens = [1, 5, 40, 127, 128, 131, 200, 700, 1500, 2100]
+    for nan_tokens in (0, 2):
+        wl = synth.build_workload(f"signed{case}", batch=len(lens), next_n=c["next_n"],
+                                  heads=c["heads"], head_dim=128, page_size=page_size,
+                                  context_lens=lens, table="permuted", topk=100,
+                                  seed=31 + case, neg_scale_blocks=0.4,
+                                  nan_scale_tokens=nan_tokens)
+        wl.out_row_stride = 2112
+        name = gpu_lib.logits_kernel(wl.batch, wl.next_n, page_size, wl.out_row_stride, wl.heads,
+                                     wl.block_tables.shape[1])
+        assert name.startswith(c["family"] + "<"), name
+        npg = (wl.context_lens.astype(np.int64) + page_size - 1) // page_size
+        scales = np.concatenate([oracle.gather_request(wl.kv_cache, wl.block_tables[b],
+                                                       int(wl.context_lens[b]), page_size, 128)[1]
+                                 for b in range(wl.batch)])
+        assert (scales < 0).any() and (scales > 0).any() and npg.sum() > 0
+        d = upload(wl)
+        out = run_logits(gpu_lib, wl, d, label=f"{name} nan_tokens={nan_tokens}")
+        ref = oracle_rows(wl)
+        worst = check_rows(wl, out, ref)
+        say(f"{name} ps={page_size} nan_tokens={nan_tokens}: worst rel err {worst:.3e}")
+        if nan_tokens == 0:
+            idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+            check_topk(idx, ref, wl.topk)
+        else:
+            assert any(np.isnan(r).any() for r in ref if r is not None)
+
+
+@pytest.mark.parametrize("case", [0, 1, 3])
+def test_negative_context_lens_count_as_zero(gpu_lib, case):
+    """Negative context lengths count as 0 (as the oracle's visible length does):
+    those requests' rows stay untouched and their top-k rows are all -1; the
+    other requests are unaffected."""
+    c = FAMILIES[case]
+    lens = [0, 300, 0, 0, 77, 1000]
+    neg = np.array([-5, 300, -1, -(2 ** 31), 77, 1000], dtype=np.int32)
+    wl = synth.build_workload("negctx", batch=len(lens), next_n=c["next_n"], heads=c["heads"],
+                              head_dim=128, page_size=64, context_lens=lens, table="permuted",
+                              topk=32, seed=77)
+    wl.out_row_stride = 1024
+    wl.context_lens = neg
+    d = upload(wl)
+    out = run_logits(gpu_lib, wl, d, label="negative context lengths")
+    ref = oracle_rows(wl)
+    check_rows(wl, out, ref)
+    check_untouched_rows(wl, out, [0, 2, 3])
+    idx = topk_gpu(gpu_lib, wl, out, ctx=d["ctx"])
+    check_topk(idx, ref, wl.topk)
+    rows = [r for b in (0, 2, 3) for r in range(b * wl.next_n, (b + 1) * wl.next_n)]
+    assert bool((idx[rows] == -1).all())
+
+
+@pytest.mark.parametrize("case", [0, 1, 3])
+def test_contexts_past_the_table_row_and_output_row(gpu_lib, case):
+    """Contexts longer than the output row and than the table row (a broken
+    precondition) are contained: a row is scored on [0, min(visible, ctx_eff)),
+    ctx_eff = min(ctx, table width * page_size, row stride), -inf up to ctx_eff,
+    and nothing is written past its row (the columns past ctx_eff and a guard
+    row after the output keep their sentinel).  The scores are those of the
+    same tokens under a context the table covers."""
+    c = FAMILIES[case]
+    ps, stride = 64, 1024
+    covered = [100, 900, 1280, 1280, 1280]        # what the 20-page table rows hold
+    true_ctx = [100, 900, 1300, 2000, 1 << 20]     # what the caller claims
+    wl = synth.build_workload("pastrow", batch=len(covered), next_n=c["next_n"],
+                              heads=c["heads"], head_dim=128, page_size=ps,
+                              context_lens=covered, table="permuted", topk=16, seed=5)
+    assert wl.block_tables.shape[1] * ps == 1280
+    ref = oracle_rows(wl)  # per-token scores over the covered tokens
+    d = upload(wl)
+    d["ctx"] = torch.tensor(true_ctx, dtype=torch.int32, device="cuda")
+    big = new_out(wl.rows + 1, stride)
+    out = big[: wl.rows]
+    say(f"[gpu] paged_mqa_logits past-row contexts {true_ctx} stride={stride} ({c['family']})")
+    gpu_lib.paged_mqa_logits(d["q"], d["kv"], d["w"], d["ctx"], d["tab"], ps, wl.next_n, out)
+    torch.cuda.synchronize()
+    bits = big.view(torch.int32).cpu().numpy()
+    vals = big.cpu().numpy()
+    assert np.all(bits[wl.rows] == SENTINEL_BITS), "guard row written"
+    nn = wl.next_n
+    for b in range(wl.batch):
+        ctx_eff = min(true_ctx[b], 1280, stride)
+        for j in range(nn):
+            r = b * nn + j
+            vis = min(max(true_ctx[b] - nn + j + 1, 0), ctx_eff)
+            want = ref[r][:vis]
+            assert len(ref[r]) >= vis
+            got = vals[r, :vis].astype(np.float64)
+            tol = 2e-4 * float(np.max(np.abs(want))) if vis else 0.0
+            assert np.all(np.abs(got - want) <= tol), f"row {r}"
+            assert np.all(bits[r, vis:ctx_eff] == np.int32(-8388608)), f"row {r}: mask"
+            assert np.all(bits[r, ctx_eff:] == SENTINEL_BITS), f"row {r}: write past ctx_eff"
+
+
+def test_binding_rejects_an_empty_table_row(gpu_lib):
+    """A [B, 0] block table holds no page: the binding refuses it (B > 0) before
+    anything is enqueued, and accepts it for an empty batch."""
+    wl = synth.build_workload("w0", batch=2, next_n=1, heads=64, head_dim=128, page_size=64,
+                              context_lens=[10, 20], table="permuted", topk=4, seed=1)
+    d = upload(wl)
+    out = new_out(2, 64)
+    with pytest.raises(ValueError):
+        gpu_lib.paged_mqa_logits(d["q"], d["kv"], d["w"], d["ctx"],
+                                 torch.empty((2, 0), dtype=torch.int64, device="cuda"), 64, 1, out)
+    assert bool((out.view(torch.int32) == SENTINEL_BITS).all())
+    e = torch.empty((0, 0), dtype=torch.int64, device="cuda")
+    gpu_lib.paged_mqa_logits(d["q"][:0], d["kv"], d["w"][:0], d["ctx"][:0], e, 64, 1,
+                             new_out(0, 64))
