@@ -16,6 +16,9 @@ the logits kernel (HBM-bound at this shape), its duration the mean of the
 events its dispatches record at kernel start and end over the same number of
 eager steps; `cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample;
 `device_copy` is a plain 512 MiB device copy (context for the HBM roofline);
+`per_config` times the other four workloads (logits and top-k launch
+durations from dispatch-recorded events over rotated input sets, their
+throughput and roofline fractions);
 `token_level_tables` times the logits on the same pools read through token-level
 tables (page_size 1); `k_cache_producer` times the K-cache producer
 (quantize_k_cache) that writes new K rows into the cache, at a decode step's rows
@@ -221,6 +224,147 @@ def measure_k_cache(lib, wl, hip, dev, sh, sizes=(16384, 131072), reps=50):
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def make_sets(wl, n_sets, dev):
+    """n_sets device copies of the workload's inputs and outputs (rotated so
+    that consecutive steps never find their pages in the last-level cache),
+    and one top-k workspace sized for the workload's longest visible row
+    (shared: the steps run in order on one stream)."""
+    import torch
+
+    import fp8_paged_mqa_block_amd as pm
+
+    sets = []
+    q = torch.from_numpy(wl.q).to(dev)
+    w = torch.from_numpy(wl.weights).to(dev)
+    ctx = torch.from_numpy(wl.context_lens).to(dev)
+    tab = torch.from_numpy(wl.block_tables).to(dev)
+    kv0 = torch.from_numpy(wl.kv_cache).to(dev)
+    for s in range(n_sets):
+        kv = kv0 if s == 0 else kv0.clone()
+        out = torch.empty((wl.rows, wl.out_row_stride), dtype=torch.float32, device=dev)
+        idx = torch.empty((wl.rows, wl.topk), dtype=torch.int32, device=dev)
+        sets.append(dict(q=q.clone(), w=w.clone(), ctx=ctx.clone(), tab=tab.clone(), kv=kv,
+                         out=out, idx=idx))
+    del kv0
+    ws_bytes = pm.topk_workspace_size(wl.rows, wl.topk, int(wl.visible_lens().max(initial=0)))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    return sets, ws, ws_bytes
+
+
+def launch_args(wl, sets, ws, ws_bytes, sh):
+    """Raw C-ABI argument tuples of the logits and top-k calls, per set."""
+    W = wl.block_tables.shape[1]
+    largs = [(d["q"].data_ptr(), d["kv"].data_ptr(), d["w"].data_ptr(), d["ctx"].data_ptr(),
+              d["tab"].data_ptr(), wl.page_size, wl.next_n, d["out"].data_ptr(),
+              wl.out_row_stride, wl.batch, wl.heads, wl.head_dim, W, sh) for d in sets]
+    targs = [(d["out"].data_ptr(), d["ctx"].data_ptr(), wl.topk, d["idx"].data_ptr(), wl.batch,
+              wl.next_n, wl.out_row_stride, ws.data_ptr() if ws_bytes else None, ws_bytes, sh)
+             for d in sets]
+    return largs, targs
+
+
+def warm_set(i, warmup, n_sets):
+    """Set of warm-up step i: the warm-up ends on the last set, so the timed
+    rotation (which starts at set 0) first reaches the sets touched longest ago."""
+    return (i - warmup) % n_sets
+
+
+def time_steps(lib, largs, targs, hip, steps, warmup):
+    """Eager steps (logits then top-k per rotated set): warm-up, then `steps`
+    steps whose kernels record dispatch events.  Returns per-launch ms lists."""
+    import torch
+
+    n = len(largs)
+    spare = [hip.create() for _ in range(4)]
+    for i in range(warmup):
+        s = warm_set(i, warmup, n)
+        assert lib.paged_mqa_logits_timed(*largs[s], spare[0], spare[1]) == 0
+        assert lib.topk_per_row_timed(*targs[s], spare[2], spare[3]) == 0
+    events = [[hip.create() for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = events[i]
+        assert lib.paged_mqa_logits_timed(*largs[i % n], e[0], e[1]) == 0
+        assert lib.topk_per_row_timed(*targs[i % n], e[2], e[3]) == 0
+    torch.cuda.synchronize()
+    time_steps.wall_s = time.perf_counter() - t0
+    logits_ms = [hip.elapsed_ms(e[0], e[1]) for e in events]
+    topk_ms = [hip.elapsed_ms(e[2], e[3]) for e in events]
+    for e in events + [spare]:
+        for h in e:
+            hip.destroy(h)
+    return logits_ms, topk_ms
+
+
+def roof_of(wl, logits_s):
+    """Binding roof of the logits launch: HBM or fp8 MFMA, by arithmetic intensity."""
+    flops = 2.0 * wl.heads * wl.head_dim * wl.scored_tokens()
+    abytes = algorithmic_bytes(wl)
+    gbps = abytes / logits_s / 1e9
+    tflops = flops / logits_s / 1e12
+    mfma_bound = flops / abytes > FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    return dict(bound="mfma" if mfma_bound else "hbm", algorithmic_bytes=abytes,
+                algorithmic_flops=flops, hbm_GBps=gbps, hbm_frac=gbps / HBM_PEAK_GBPS,
+                tflops=tflops, mfma_frac=tflops / FP8_PEAK_TFLOPS,
+                frac=(tflops / FP8_PEAK_TFLOPS) if mfma_bound else (gbps / HBM_PEAK_GBPS))
+
+
+def measure_config(lib, cfg, hip, dev, sh, steps=20, warmup=5):
+    """One workload's logits and top-k launches, timed eagerly over rotated sets
+    (16 for the small decode shape, 3 for the large ones, whose single step
+    already exceeds the last-level cache)."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    t0 = time.perf_counter()
+    wl = synth.make_config(cfg)
+    gen_s = time.perf_counter() - t0
+    n_sets = 16 if cfg == 1 else 3
+    sets, ws, ws_bytes = make_sets(wl, n_sets, dev)
+    largs, targs = launch_args(wl, sets, ws, ws_bytes, sh)
+    torch.cuda.synchronize()
+    logits_ms, topk_ms = time_steps(lib, largs, targs, hip, steps, warmup)
+    lg_s = float(np.mean(logits_ms)) * 1e-3
+    tk_s = float(np.mean(topk_ms)) * 1e-3
+    roof = roof_of(wl, lg_s)
+    tbytes = topk_bytes(wl)
+    scored = wl.scored_tokens()
+    res = {
+        "workload": wl.name, "batch": wl.batch, "next_n": wl.next_n, "heads": wl.heads,
+        "page_size": wl.page_size, "topk": wl.topk, "scored_tokens": scored,
+        "kernel": logits_kernel_name(wl),
+        "logits_us": {"mean": lg_s * 1e6, "median": float(np.median(logits_ms)) * 1e3},
+        "topk_us": {"mean": tk_s * 1e6, "median": float(np.median(topk_ms)) * 1e3},
+        "step_us": (lg_s + tk_s) * 1e6,
+        "tokens_per_s": scored / (lg_s + tk_s),
+        "logits_tokens_per_s": scored / lg_s,
+        "tflops": roof["tflops"],
+        "logits_roofline": roof,
+        "topk_GBps": tbytes / tk_s / 1e9,
+        "topk_hbm_frac": tbytes / tk_s / 1e9 / HBM_PEAK_GBPS,
+        "topk_algorithmic_bytes": tbytes,
+        "topk_workspace_bytes": ws_bytes,
+        "rotated_sets": n_sets, "launches": steps, "generate_s": gen_s,
+    }
+    del sets, ws, largs, targs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, min_seconds=10.0, max_reps=400):
     import oracle
     from threadpoolctl import threadpool_info
@@ -240,6 +384,7 @@ def cpu_baseline(wl, min_seconds=10.0, max_reps=400):
         "value": wl.scored_tokens() * reps / el,
         "unit": "tokens/s",
         "cores": int(threads),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"the whole {wl.name} workload (logits + top-k, {wl.scored_tokens()} scored tokens) "
                   f"run {reps}x in {el:.1f} s, numpy fp64 on {threads} BLAS threads",
@@ -257,6 +402,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the step (no copy, token-level or producer measurements): "
                          "for profiler runs whose per-kernel figures must cover the step alone")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip timing the other workloads")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -283,22 +430,12 @@ def main():
           f"ps={wl.page_size} scored={wl.scored_tokens()} sets={args.sets}", file=sys.stderr,
           flush=True)
 
-    sets = []
-    q = torch.from_numpy(wl.q).to(dev)
-    w = torch.from_numpy(wl.weights).to(dev)
-    ctx = torch.from_numpy(wl.context_lens).to(dev)
-    tab = torch.from_numpy(wl.block_tables).to(dev)
-    kv0 = torch.from_numpy(wl.kv_cache).to(dev)
-    for s in range(args.sets):
-        kv = kv0 if s == 0 else kv0.clone()
-        out = torch.empty((rows, stride), dtype=torch.float32, device=dev)
-        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
-        sets.append(dict(q=q.clone(), w=w.clone(), ctx=ctx.clone(), tab=tab.clone(), kv=kv,
-                         out=out, idx=idx))
+    sets, ws, ws_bytes = make_sets(wl, args.sets, dev)
     # check once through the binding, then launch through the raw C ABI in the loop
     pm.paged_mqa_logits(sets[0]["q"].view(torch.float8_e4m3fn), sets[0]["kv"], sets[0]["w"],
                         sets[0]["ctx"], sets[0]["tab"], wl.page_size, wl.next_n, sets[0]["out"])
-    pm.topk_per_row(sets[0]["out"], sets[0]["ctx"], k, sets[0]["idx"], next_n=wl.next_n)
+    pm.topk_per_row(sets[0]["out"], sets[0]["ctx"], k, sets[0]["idx"], next_n=wl.next_n,
+                    workspace=ws[:ws_bytes])
     torch.cuda.synchronize()
 
     if args.calibrate_copy_mib:
@@ -315,41 +452,14 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     sh = int(stream.cuda_stream)
-    W = wl.block_tables.shape[1]
-    largs = [(d["q"].data_ptr(), d["kv"].data_ptr(), d["w"].data_ptr(), d["ctx"].data_ptr(),
-              d["tab"].data_ptr(), wl.page_size, wl.next_n, d["out"].data_ptr(), stride,
-              wl.batch, wl.heads, wl.head_dim, W, sh) for d in sets]
-    targs = [(d["out"].data_ptr(), d["ctx"].data_ptr(), k, d["idx"].data_ptr(), wl.batch,
-              wl.next_n, stride, sh) for d in sets]
-    logits_fn, topk_fn = lib.paged_mqa_logits_timed, lib.topk_per_row_timed
+    largs, targs = launch_args(wl, sets, ws, ws_bytes, sh)
     hip = HipEvents()
-
-    def step(i, ev):
-        st = logits_fn(*largs[i % len(largs)], ev[0], ev[1])
-        st |= topk_fn(*targs[i % len(targs)], ev[2], ev[3])
-        return st
-
-    spare = [hip.create() for _ in range(4)]
-    for i in range(args.warmup):
-        assert step(i, spare) == 0
-    torch.cuda.synchronize()
 
     # Kernel durations: dispatch-recorded start/end events of every launch over
     # `steps` eager steps (the same rotated inputs).
-    events = [[hip.create() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    bad = 0
-    for i in range(args.steps):
-        bad |= step(i, events[i])
-    torch.cuda.synchronize()
-    eager_elapsed = time.perf_counter() - t0
-    assert bad == 0
-    logits_ms = [hip.elapsed_ms(e[0], e[1]) for e in events]
-    topk_ms = [hip.elapsed_ms(e[2], e[3]) for e in events]
-    for e in events + [spare]:
-        for h in e:
-            hip.destroy(h)
+    logits_ms, topk_ms = time_steps(lib, largs, targs, hip, args.steps, args.warmup)
+    eager_elapsed = time_steps.wall_s
 
     # Step throughput: W warm-up steps, then exactly K timed steps, each a
     # sequence of steps over the rotated input sets (logits then top-k each)
@@ -358,18 +468,22 @@ def main():
     # back to back.
     cap = torch.cuda.Stream(dev)
 
-    def capture(n_steps):
+    def capture(set_of_step, n_steps):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
                 csh = int(torch.cuda.current_stream(dev).cuda_stream)
                 for i in range(n_steps):
-                    a = list(largs[i % len(sets)]); a[-1] = csh
-                    t = list(targs[i % len(sets)]); t[-1] = csh
+                    a = list(largs[set_of_step(i)]); a[-1] = csh
+                    t = list(targs[set_of_step(i)]); t[-1] = csh
                     assert lib.paged_mqa_logits(*a) == 0 and lib.topk_per_row(*t) == 0
         return g
 
-    warm_graph, timed_graph = capture(max(args.warmup, 1)), capture(args.steps)
+    # the warm-up ends on the last set, so the timed steps (sets 0, 1, ...)
+    # start on the sets touched longest ago
+    nw = max(args.warmup, 1)
+    warm_graph = capture(lambda i: warm_set(i, nw, len(sets)), nw)
+    timed_graph = capture(lambda i: i % len(sets), args.steps)
     torch.cuda.synchronize()
     warm_graph.replay()
     torch.cuda.synchronize()
@@ -422,18 +536,30 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "next_n": wl.next_n,
                    "heads": wl.heads, "head_dim": wl.head_dim, "page_size": wl.page_size,
                    "context_lens": "U[1,8192]" if args.config == 2 else "see workload",
-                   "topk": k, "scored_tokens_per_step": scored, "rotated_input_sets": args.sets},
+                   "topk": k, "scored_tokens_per_step": scored, "rotated_input_sets": args.sets,
+                   "topk_workspace_bytes": ws_bytes},
         "tflops": flops * graph_steps / elapsed / 1e12,
         "eager_ms_per_step": eager_elapsed * 1e3 / args.steps,
         "logits_us": {"mean": lg_avg_s * 1e6, "median": float(np.median(logits_ms)) * 1e3},
         "topk_us": {"mean": float(np.mean(topk_ms)) * 1e3, "median": float(np.median(topk_ms)) * 1e3},
         "logits_tflops": flops / lg_avg_s / 1e12,
+        "topk_GBps": topk_bytes(wl) / (float(np.mean(topk_ms)) * 1e-3) / 1e9,
+        "topk_hbm_frac": topk_bytes(wl) / (float(np.mean(topk_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "roofline": roof,
     }
     if not args.no_extras:
         res["device_copy"] = measure_copy(dev)
         res["token_level_tables"] = measure_token_level(lib, wl, sets, hip, sh)
         res["k_cache_producer"] = measure_k_cache(lib, wl, hip, dev, sh)
+    if not args.no_per_config:
+        del sets, ws, largs, targs
+        torch.cuda.empty_cache()
+        res["per_config"] = {}
+        for cfg in (1, 3, 4, 5):
+            if cfg == args.config:
+                continue
+            print(f"[bench] per_config: workload {cfg}", file=sys.stderr, flush=True)
+            res["per_config"][synth.CONFIG_NAMES[cfg]] = measure_config(lib, cfg, hip, dev, sh)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res, default=lambda o: o.item() if hasattr(o, "item") else str(o)), flush=True)

@@ -21,6 +21,7 @@ __all__ = [
     "logits_kernel",
     "paged_mqa_logits",
     "topk_per_row",
+    "topk_workspace_size",
     "check_inputs",
     "quantize_k_cache",
     "EXPORTS",
@@ -32,14 +33,14 @@ _lib: Optional[ctypes.CDLL] = None
 
 # Every symbol include/pmqa.h declares.
 EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "topk_per_row", "topk_per_row_timed",
-           "pmqa_check_inputs", "quantize_k_cache", "quantize_k_cache_timed",
-           "pmqa_status_string", "pmqa_version", "pmqa_logits_kernel")
+           "topk_per_row_workspace_size", "pmqa_check_inputs", "quantize_k_cache",
+           "quantize_k_cache_timed", "pmqa_status_string", "pmqa_version", "pmqa_logits_kernel")
 
 # pmqa_dtype codes of the K rows quantize_k_cache accepts
 _K_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 _STATUS = {0: "PMQA_OK", 1: "PMQA_ERR_NULL", 2: "PMQA_ERR_SHAPE", 3: "PMQA_ERR_UNSUPPORTED",
-           4: "PMQA_ERR_ALIGNMENT", 5: "PMQA_ERR_HIP"}
+           4: "PMQA_ERR_WORKSPACE", 5: "PMQA_ERR_HIP", 6: "PMQA_ERR_ALIGNMENT"}
 
 
 class PmqaError(RuntimeError):
@@ -79,9 +80,11 @@ def load_library() -> ctypes.CDLL:
     lib.paged_mqa_logits_timed.restype = ctypes.c_int
     lib.paged_mqa_logits_timed.argtypes = lib.paged_mqa_logits.argtypes + [vp, vp]
     lib.topk_per_row.restype = ctypes.c_int
-    lib.topk_per_row.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp]
+    lib.topk_per_row.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp, ctypes.c_size_t, vp]
     lib.topk_per_row_timed.restype = ctypes.c_int
     lib.topk_per_row_timed.argtypes = lib.topk_per_row.argtypes + [vp, vp]
+    lib.topk_per_row_workspace_size.restype = ctypes.c_size_t
+    lib.topk_per_row_workspace_size.argtypes = [c_i32, c_i32, c_i64]
     lib.pmqa_check_inputs.restype = ctypes.c_int
     lib.pmqa_check_inputs.argtypes = [vp, vp, c_i32, c_i32, c_i64, c_i64, c_i64, vp, vp]
     lib.quantize_k_cache.restype = ctypes.c_int
@@ -171,9 +174,23 @@ def paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Ten
     return out
 
 
+def topk_workspace_size(rows: int, k: int, max_row_len: int) -> int:
+    """Workspace bytes with which topk_per_row splits rows of up to max_row_len
+    visible scores fully (host only; see topk_per_row_workspace_size in include/pmqa.h)."""
+    return int(load_library().topk_per_row_workspace_size(int(rows), int(k), int(max_row_len)))
+
+
 def topk_per_row(logits: torch.Tensor, context_lens: torch.Tensor, k: int, out_idx: torch.Tensor,
-                 next_n: int = 1, stream=None) -> torch.Tensor:
-    """Enqueue the per-row top-k; writes ``out_idx`` [B*next_n, k] int32 in place and returns it."""
+                 next_n: int = 1, workspace: Optional[torch.Tensor] = None,
+                 max_row_len: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Enqueue the per-row top-k; writes ``out_idx`` [B*next_n, k] int32 in place and returns it.
+
+    ``workspace`` is a device uint8 tensor the selection may use for the
+    candidates of long rows.  When None, one is allocated (torch's caching
+    allocator) of topk_workspace_size(rows, k, max_row_len), max_row_len
+    defaulting to the row stride; pass an explicit tensor (any size, 0
+    included) to control the memory.
+    """
     lib = load_library()
     for name, t in (("logits", logits), ("context_lens", context_lens), ("out_idx", out_idx)):
         _need(t.is_cuda, f"{name} must be a device tensor")
@@ -185,8 +202,16 @@ def topk_per_row(logits: torch.Tensor, context_lens: torch.Tensor, k: int, out_i
     _need(logits.shape[0] == B * next_n, "logits must have B*next_n rows")
     _need(out_idx.dtype == torch.int32 and out_idx.is_contiguous()
           and tuple(out_idx.shape) == (B * next_n, k), "out_idx must be contiguous int32 [B*next_n, k]")
+    if workspace is None:
+        size = topk_workspace_size(B * next_n, k, logits.shape[1] if max_row_len is None else max_row_len)
+        workspace = torch.empty(max(size, 1), dtype=torch.uint8, device=logits.device)
+    _need(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.is_contiguous(),
+          "workspace must be a contiguous uint8 device tensor")
+    nbytes = int(workspace.numel())
     st = lib.topk_per_row(logits.data_ptr(), context_lens.data_ptr(), int(k), out_idx.data_ptr(),
-                          int(B), int(next_n), int(logits.shape[1]), _stream_handle(out_idx, stream))
+                          int(B), int(next_n), int(logits.shape[1]),
+                          workspace.data_ptr() if nbytes else None, nbytes,
+                          _stream_handle(out_idx, stream))
     _check("topk_per_row", st)
     return out_idx
 

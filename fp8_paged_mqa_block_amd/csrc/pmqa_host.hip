@@ -63,6 +63,21 @@ pmqa_status check_logits_sizes(int32_t batch, int32_t next_n, int32_t page_size,
 
 }  // namespace
 
+namespace pmqa {
+
+int64_t topk_segment_grid(int64_t rows, int32_t k, int64_t max_row_len, uint64_t workspace_bytes) {
+  if (rows < 1 || k < 1) return 1;
+  if (max_row_len > INT32_MAX) max_row_len = INT32_MAX;
+  int64_t g = (max_row_len + kTopkSegmentKeys - 1) / kTopkSegmentKeys;  // segments a row needs
+  const int64_t merge_cap = kTopkMergeKeys / k;  // the merge holds segments * k candidates
+  if (g > merge_cap) g = merge_cap;
+  const uint64_t per_segment = (uint64_t)rows * (uint64_t)k * 8u;  // candidates of every row
+  if ((uint64_t)g > workspace_bytes / per_segment) g = (int64_t)(workspace_bytes / per_segment);
+  return g > 1 ? g : 1;
+}
+
+}  // namespace pmqa
+
 extern "C" {
 
 const char* pmqa_status_string(pmqa_status status) {
@@ -71,8 +86,9 @@ const char* pmqa_status_string(pmqa_status status) {
     case PMQA_ERR_NULL: return "null pointer argument";
     case PMQA_ERR_SHAPE: return "size or stride out of range";
     case PMQA_ERR_UNSUPPORTED: return "unsupported shape or dtype (num_heads 16/32/64/128, head_dim 128, k fp32 or bf16)";
-    case PMQA_ERR_ALIGNMENT: return "pointer not aligned as required";
+    case PMQA_ERR_WORKSPACE: return "workspace missing (NULL with a nonzero size)";
     case PMQA_ERR_HIP: return "HIP runtime error at launch";
+    case PMQA_ERR_ALIGNMENT: return "pointer not aligned as required";
   }
   return "unknown status";
 }
@@ -170,14 +186,18 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
 
 pmqa_status topk_impl(const float* logits, const int32_t* context_lens, int32_t k,
                       int32_t* out_idx, int32_t batch, int32_t next_n, int64_t logits_row_stride,
-                      void* stream, const pmqa::LaunchTiming& tm) {
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      const pmqa::LaunchTiming& tm) {
   if (batch < 0 || next_n < 1 || logits_row_stride < 1) return PMQA_ERR_SHAPE;
   if (k < 1 || k > 2048) return PMQA_ERR_SHAPE;
   if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
+  if (workspace_bytes > 0 && !workspace) return PMQA_ERR_WORKSPACE;
   if (batch == 0) return PMQA_OK;
   if (!logits || !context_lens || !out_idx) return PMQA_ERR_NULL;
-  if (!aligned(logits, 4) || !aligned(context_lens, 4) || !aligned(out_idx, 4))
+  if (!aligned(logits, 4) || !aligned(context_lens, 4) || !aligned(out_idx, 4) ||
+      (workspace_bytes > 0 && !aligned(workspace, 16)))
     return PMQA_ERR_ALIGNMENT;
+  const int64_t rows = (int64_t)batch * next_n;
   pmqa::TopkParams p{};
   p.logits = logits;
   p.ctx = context_lens;
@@ -186,6 +206,12 @@ pmqa_status topk_impl(const float* logits, const int32_t* context_lens, int32_t 
   p.batch = batch;
   p.next_n = next_n;
   p.k = k;
+  p.seg_grid = (int32_t)pmqa::topk_segment_grid(rows, k, logits_row_stride, workspace_bytes);
+  if (p.seg_grid > 1) {
+    const int64_t slots = rows * p.seg_grid * k;
+    p.cand_val = static_cast<float*>(workspace);
+    p.cand_idx = reinterpret_cast<int32_t*>(p.cand_val + slots);
+  }
   hipError_t e = pmqa::launch_topk(p, tm, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
 }
@@ -246,17 +272,24 @@ pmqa_status paged_mqa_logits_timed(const void* q, const void* kv_cache, const fl
 
 pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,
                          int32_t* out_idx, int32_t batch, int32_t next_n,
-                         int64_t logits_row_stride, void* stream) {
-  return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, stream,
-                   pmqa::LaunchTiming{});
+                         int64_t logits_row_stride, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, workspace,
+                   workspace_bytes, stream, pmqa::LaunchTiming{});
 }
 
 pmqa_status topk_per_row_timed(const float* logits, const int32_t* context_lens, int32_t k,
                                int32_t* out_idx, int32_t batch, int32_t next_n,
-                               int64_t logits_row_stride, void* stream, void* start_event,
-                               void* stop_event) {
-  return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, stream,
-                   timing(start_event, stop_event));
+                               int64_t logits_row_stride, void* workspace, size_t workspace_bytes,
+                               void* stream, void* start_event, void* stop_event) {
+  return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, workspace,
+                   workspace_bytes, stream, timing(start_event, stop_event));
+}
+
+size_t topk_per_row_workspace_size(int32_t rows, int32_t k, int64_t max_row_len) {
+  if (rows < 0 || k < 1 || k > 2048 || max_row_len < 0) return 0;
+  const int64_t g = pmqa::topk_segment_grid(rows, k, max_row_len, UINT64_MAX);
+  return g > 1 ? (size_t)rows * (size_t)g * (size_t)k * 8u : 0u;
 }
 
 pmqa_status quantize_k_cache(const void* k, int32_t k_dtype, const int64_t* slot_mapping,

@@ -59,15 +59,29 @@ void persistent_geometry(int heads, int rows_per_wave, int* waves, int* ring);
 hipError_t launch_logits(const LogitsParams& p, const LogitsShape& sh, int heads,
                          const LaunchTiming& tm, hipStream_t stream);
 
+// Scores one top-k workgroup selects from registers: a row longer than this is
+// split into segments of at most this many scores (while the workspace has
+// room for their candidates), and a row's merge takes at most this many
+// candidates (segments * k).
+constexpr int kTopkSegmentKeys = 16384;
+constexpr int kTopkMergeKeys = 16384;
+
 struct TopkParams {
   const float* logits;
   const int32_t* ctx;
   int32_t* out_idx;
+  float* cand_val;         // workspace: [rows, seg_grid, k] candidate scores
+  int32_t* cand_idx;       // workspace: [rows, seg_grid, k] candidate indices
   int64_t row_stride;
   int32_t batch;
   int32_t next_n;
   int32_t k;
+  int32_t seg_grid;        // most segments a row is split into (1: no split)
 };
+
+// Most segments a row of up to max_row_len scores is split into, given the
+// workspace bytes for its candidates (0 bytes: 1, no split).
+int64_t topk_segment_grid(int64_t rows, int32_t k, int64_t max_row_len, uint64_t workspace_bytes);
 
 hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t stream);
 

@@ -4,35 +4,44 @@
 // #4244, first paragraph): for each row r, the indices of the k largest scores
 // among its visible tokens [0, visible(r)), -1 in the slots left over.
 //
-// One 1024-thread workgroup per row runs an exact select on order-preserving
-// 32-bit keys.  The design keeps every step off long LDS round-trip chains,
-// which dominate at these sizes:
-//  * the row is loaded once into registers (up to 16 keys a thread; its first
-//    8192 scores are loaded before the row length is read); longer rows stream
-//    through registers chunk by chunk in every pass, the next chunk's loads in
-//    flight while the current one is processed;
-//  * on a row held in registers whose scores are all finite, the first pass
-//    buckets by value, linearly between the row's smallest and largest score
+// Work split.  A row of up to 16384 scores is selected by one 1024-thread
+// workgroup.  A longer row is cut into nseg nearly equal segments (at most
+// the grid's second dimension, which the caller's workspace bounds), each
+// selected by its own workgroup into k candidates (score, index) in the
+// workspace; a second launch then selects the row's top k among its nseg * k
+// candidates.  This is exact: every key of the row's top k is in its
+// segment's top k under the same order (score descending, index ascending),
+// and for any one score a segment lists its keys in index order, so taking
+// equal candidates in list order still takes the lowest indices.  Only the
+// visible scores [0, visible) are read.
+//
+// One workgroup's exact select on order-preserving 32-bit keys keeps every
+// step off long LDS round-trip chains, which dominate at these sizes:
+//  * the keys are loaded once into registers (up to 16 a thread); longer
+//    segments (a workspace too small to split the row further) stream
+//    through registers chunk by chunk in every pass, the next chunk's loads
+//    in flight while the current one is processed;
+//  * on keys held in registers whose scores are all finite, the first pass
+//    buckets by value, linearly between the smallest and largest score
 //    (monotone, so still exact): on bell-shaped scores the bucket holding the
 //    k-th key keeps a few dozen keys, where a radix digit (mostly sign and
-//    exponent bits) keeps hundreds.  Streamed rows keep radix digits: there
+//    exponent bits) keeps hundreds.  Streamed keys keep radix digits: there
 //    one CU handles up to 128K keys per pass and the bucket's arithmetic costs
 //    more than the pass it saves;
 //  * radix passes take 11-bit digits (2048 bins) of the keys in the threshold
-//    bin, starting below the bits every key of the row shares, so scores in
-//    one binade still spread over the bins instead of piling onto one LDS
-//    address;
+//    bin, starting below the bits every key shares, so scores in one binade
+//    still spread over the bins instead of piling onto one LDS address;
 //  * the passes stop as soon as the threshold bin is taken whole, or holds at
-//    most 128 keys (256 for a streamed row, where a pass costs a full read):
-//    those are then gathered in row order and ranked against each other,
-//    each candidate compared as one 64-bit value (key above inverted
-//    position) by 8 lanes (4 for a streamed row), so all 16 waves rank;
+//    most 128 keys (256 when streamed, where a pass costs a full read): those
+//    are then gathered in order and ranked against each other, each candidate
+//    compared as one 64-bit value (key above inverted position) by 8 lanes (4
+//    when streamed), so all 16 waves rank;
 //  * each pass has two barriers: after the histogram, and after the per-wave
 //    bin totals; sums, prefix sums and min/max inside a wave use DPP row
 //    operations and lane reads, not LDS shuffles;
-//  * the final pass writes the indices at ordered positions (wave-major, then
-//    key order), so the output is deterministic and, among keys equal to the
-//    threshold, the lowest indices are taken.
+//  * the final pass writes at ordered positions (wave-major, then key order),
+//    so the output is deterministic and, among keys equal to the threshold,
+//    the first ones in order (the lowest indices) are taken.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -79,15 +88,20 @@ struct TopkShared {
   int32_t cand_idx[kCandCap];
 };
 
-// Keys of one chunk: thread (wave w, lane l) holds key j of the chunk at row
-// index chunk_base + w*64*KPT + j*64 + l (coalesced per j, wave-major order).
-template <int KPT>
+// Keys of one chunk: thread (wave w, lane l) holds key j of the chunk at
+// position chunk_base + w*64*KPT + j*64 + l (coalesced per j, wave-major
+// order).  With IDX the chunk also carries each key's index in the row (the
+// merge selects among candidates that came from anywhere in the row);
+// otherwise a key's index is its position.
+template <int KPT, bool IDX = false>
 struct Chunk {
   uint32_t key[KPT];
+  int32_t idx[IDX ? KPT : 1];
   int valid;  // keys j < valid are inside the row
 
   __device__ __forceinline__ void load(const float* __restrict__ row, int n, int64_t base) {
-    // base = chunk start + this thread's first index
+    // base = chunk start + this thread's first position; positions past the
+    // row re-read its last score (no extra cache line) and are never used
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int64_t i = base + 64 * j;
@@ -96,18 +110,13 @@ struct Chunk {
     set_valid(n, base);
   }
 
-  // The chunk's raw scores, loaded before the row length is known: the caller
-  // guarantees that the whole span lies inside the row's stride.  finish()
-  // turns them into keys once the length is known.
-  __device__ __forceinline__ void load_span(const float* __restrict__ row, int64_t base) {
+  __device__ __forceinline__ void load_idx(const int32_t* __restrict__ ids, int n, int64_t base) {
+    static_assert(IDX, "a chunk without indices");
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = __float_as_uint(row[base + 64 * j]);
-  }
-
-  __device__ __forceinline__ void finish(int n, int64_t base) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = order_key(__uint_as_float(key[j]));
-    set_valid(n, base);
+    for (int j = 0; j < KPT; ++j) {
+      const int64_t i = base + 64 * j;
+      idx[j] = ids[i < n ? i : n - 1];
+    }
   }
 
   __device__ __forceinline__ void set_valid(int n, int64_t base) {
@@ -115,12 +124,33 @@ struct Chunk {
     const int64_t left = (int64_t)n - base;
     valid = left <= 0 ? 0 : (int)min<int64_t>((left + 63) / 64, KPT);
   }
+
+  // the index of key j, at position pos
+  __device__ __forceinline__ int32_t index(int j, int64_t pos) const {
+    if constexpr (IDX) return idx[j];
+    else return (int32_t)pos;
+  }
 };
 
 // The float a key encodes (inverse of order_key; -0 comes back as +0).
 __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
+
+// Where a selected key goes: slot in [0, k) of `idx` receives its index in
+// the row (a segment starts at position `base` of the row) and, when `val` is
+// set, slot of `val` its score (-0 comes back as +0, the same key): a
+// segment's top k as candidates of the row's merge.  One type for both uses,
+// so that each key layout is compiled once per kernel.
+struct SelectOut {
+  int32_t* idx;
+  float* val;
+  int32_t base;
+  __device__ __forceinline__ void put(uint32_t slot, int32_t i, uint32_t key) const {
+    idx[slot] = base + i;
+    if (val) val[slot] = key_value(key);
+  }
+};
 
 // A first pass over buckets linear in the score, for rows whose scores are all
 // finite: bucket(x) = min(floor((x - lo) * scale), 2047) with lo the row's
@@ -161,10 +191,11 @@ struct Buckets {
 // above the threshold when its bucket is higher, or its bucket is the
 // threshold bucket and its fixed bits are higher; it is in the threshold bin
 // when both are equal.
-template <int KPT, bool STREAM>
+template <int KPT, bool STREAM, bool IDX, class Out>
 __device__ __forceinline__ void select_row(const float* __restrict__ row, int n, int k,
-                                           int32_t* __restrict__ out, TopkShared& sh,
-                                           Chunk<KPT>& ch) {
+                                           const Out& out, TopkShared& sh,
+                                           Chunk<KPT, IDX>& ch) {
+  static_assert(!(STREAM && IDX), "streamed keys carry no indices");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -176,7 +207,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   // entry.  A streamed row alternates two register chunks so that the next
   // chunk's loads are in flight while the current one is processed (a row of
   // 128K keys is 8 chunks per pass, each load a full memory latency).
-  Chunk<KPT> nx;
+  Chunk<KPT, IDX> nx;
   auto for_chunks = [&](auto&& body) {
     if constexpr (!STREAM) {
       body(ch, 0);
@@ -196,7 +227,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
 
   // ---- the row's largest and smallest key ----
   uint32_t kmax = 0u, kmin = ~0u;
-  for_chunks([&](const Chunk<KPT>& cc, int) {
+  for_chunks([&](const Chunk<KPT, IDX>& cc, int) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       if (j < cc.valid) {
@@ -240,7 +271,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     const uint32_t dmask = (1u << width) - 1u;
     uint32_t* h = sh.hist[buf];
     rewind();
-    for_chunks([&](const Chunk<KPT>& cc, int) {
+    for_chunks([&](const Chunk<KPT, IDX>& cc, int) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const uint32_t key = cc.key[j];
@@ -321,7 +352,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   const uint32_t first_eq = (uint32_t)(k - remaining);
   uint32_t run_a = 0, run_e = 0;
   rewind();
-  for_chunks([&](const Chunk<KPT>& cc, int c) {
+  for_chunks([&](const Chunk<KPT, IDX>& cc, int c) {
     bool is_a[KPT], is_e[KPT];
     uint32_t ca = 0, ce = 0;
 #pragma unroll
@@ -358,15 +389,15 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     for (int j = 0; j < KPT; ++j) {
       const uint64_t ma = __ballot(fa[j] != 0);
       const uint64_t me = __ballot(fe[j] != 0);
-      const int32_t idx = (int32_t)(base + 64 * j);
-      if (fa[j]) out[off_a + (uint32_t)lane_rank(ma)] = idx;
+      const int32_t idx = cc.index(j, base + 64 * j);
+      if (fa[j]) out.put(off_a + (uint32_t)lane_rank(ma), idx, cc.key[j]);
       if (fe[j]) {
         const uint32_t rank = off_e + (uint32_t)lane_rank(me);
         if (rank_bin) {
           sh.cand_key[rank] = cc.key[j];
           sh.cand_idx[rank] = idx;
         } else if (rank < (uint32_t)remaining) {
-          out[first_eq + rank] = idx;
+          out.put(first_eq + rank, idx, cc.key[j]);
         }
       }
       off_a += (uint32_t)__popcll(ma);
@@ -404,12 +435,50 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   }
 #pragma unroll
   for (int d = 1; d < T; d <<= 1) rank += (uint32_t)__shfl_xor((int)rank, d);
-  if (part == 0 && t < nc && rank < (uint32_t)remaining) out[first_eq + rank] = sh.cand_idx[t];
+  if (part == 0 && t < nc && rank < (uint32_t)remaining)
+    out.put(first_eq + rank, sh.cand_idx[t], sh.cand_key[t]);
 }
 
-// The row pointer, stride, context lengths and next_n come first as scalar
-// arguments: the dispatch preloads them into SGPRs (the build asks for up to
-// 16 preloaded dwords), so the row and context-length loads issue at once.
+// Visible scores of row r (a row never reads past its stride).
+__device__ __forceinline__ int row_len(const int32_t* __restrict__ ctx_lens, int r, int next_n,
+                                       int64_t row_stride) {
+  const int b = r / next_n;
+  const int j = r - b * next_n;
+  const int ctx = max(ctx_lens[b], 0);
+  const int n = min(max(ctx - next_n + j + 1, 0), ctx);
+  return (int64_t)n > row_stride ? (int)row_stride : n;
+}
+
+// Segments of a row of n > k scores: one per kTopkSegmentKeys scores, at most
+// `grid` (the launch's second dimension, which the host bounds by the
+// workspace and by the merge's capacity).
+__device__ __forceinline__ int row_segments(int n, int grid) {
+  return min((n + kTopkSegmentKeys - 1) / kTopkSegmentKeys, grid);
+}
+
+// Selects n keys at `row` (positions 0..n-1) into `out`, with the register
+// layout their count calls for.
+__device__ __forceinline__ void select_keys(const float* __restrict__ row, int n, int k,
+                                            const SelectOut& out, TopkShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (n <= kThreads * kSmallKeys) {
+    Chunk<kSmallKeys> ch;
+    ch.load(row, n, (int64_t)wave * 64 * kSmallKeys + lane);
+    select_row<kSmallKeys, false>(row, n, k, out, sh, ch);
+  } else {
+    Chunk<kLargeKeys> ch;
+    ch.load(row, n, (int64_t)wave * 64 * kLargeKeys + lane);
+    if (n <= kThreads * kLargeKeys) select_row<kLargeKeys, false>(row, n, k, out, sh, ch);
+    else select_row<kLargeKeys, true>(row, n, k, out, sh, ch);
+  }
+}
+
+// Stage 1.  Workgroup (r, s) selects segment s of row r: the whole row when
+// it has one segment (the result goes straight to out_idx), otherwise k
+// candidates of the segment into the workspace.  The row pointer, stride,
+// context lengths and next_n come first as scalar arguments: the dispatch
+// preloads them into SGPRs (the build asks for up to 16 preloaded dwords), so
+// the context-length load issues at once.
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ logits,
                                                        int64_t row_stride,
                                                        const int32_t* __restrict__ ctx_lens,
@@ -417,53 +486,88 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   __shared__ TopkShared sh;
 
   const int r = blockIdx.x;
-  const int b = r / next_n;
-  const int j = r - b * next_n;
-  const float* row = logits + (int64_t)r * row_stride;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // When the row's stride spans the first size class, its scores are loaded
-  // before the row length is known, so that the context-length read and this
-  // load overlap instead of running back to back; rows of another class
-  // discard them.
-  const bool early = row_stride >= (int64_t)kThreads * kSmallKeys;
-  const int64_t base_small = (int64_t)wave * 64 * kSmallKeys + lane;
-  Chunk<kSmallKeys> first;
-  if (early) first.load_span(row, base_small);
-
-  const int ctx = max(ctx_lens[b], 0);
-  int n = min(max(ctx - next_n + j + 1, 0), ctx);
-  if ((int64_t)n > row_stride) n = (int)row_stride;
+  const int s = blockIdx.y;
+  const int n = row_len(ctx_lens, r, next_n, row_stride);
   const int k = p.k;
   int32_t* out = p.out_idx + (int64_t)r * k;
-
   if (n <= k) {
-    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
+    if (s == 0)
+      for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
     return;
   }
-  if (n <= kThreads * kSmallKeys) {
-    if (early) first.finish(n, base_small);
-    else first.load(row, n, base_small);
+  const int nseg = row_segments(n, (int)gridDim.y);
+  if (s >= nseg) return;
+  // a row of one segment selects straight into out_idx; otherwise nearly
+  // equal segments (each holds more than k scores: at least half a segment's
+  // worth, and k <= 2048) select k candidates each into the workspace
+  const int64_t s0 = (int64_t)n * s / nseg, s1 = (int64_t)n * (s + 1) / nseg;
+  const int64_t slot = ((int64_t)r * gridDim.y + s) * k;
+  const SelectOut so = nseg == 1 ? SelectOut{out, nullptr, 0}
+                                 : SelectOut{p.cand_idx + slot, p.cand_val + slot, (int32_t)s0};
+  select_keys(logits + (int64_t)r * row_stride + s0, (int)(s1 - s0), k, so, sh);
+}
+
+// Stage 2.  Workgroup r selects the top k of row r among its segments'
+// nseg * k candidates (at most kTopkMergeKeys: the host caps the segments),
+// held in registers with their indices.  Rows of one segment or none were
+// finished in stage 1.
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __restrict__ ctx_lens,
+                                                             int32_t next_n, int64_t row_stride,
+                                                             TopkParams p) {
+  __shared__ TopkShared sh;
+
+  const int r = blockIdx.x;
+  const int n = row_len(ctx_lens, r, next_n, row_stride);
+  const int k = p.k;
+  if (n <= k) return;
+  const int nseg = row_segments(n, p.seg_grid);
+  if (nseg < 2) return;
+  const int m = nseg * k;
+  const int64_t slot = (int64_t)r * p.seg_grid * k;
+  const float* cv = p.cand_val + slot;
+  const int32_t* ci = p.cand_idx + slot;
+  const SelectOut out{p.out_idx + (int64_t)r * k, nullptr, 0};
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (m <= kThreads * kSmallKeys) {
+    Chunk<kSmallKeys, true> ch;
+    const int64_t base = (int64_t)wave * 64 * kSmallKeys + lane;
+    ch.load(cv, m, base);
+    ch.load_idx(ci, m, base);
+    select_row<kSmallKeys, false>(cv, m, k, out, sh, ch);
+  } else {
+    Chunk<kLargeKeys, true> ch;
+    const int64_t base = (int64_t)wave * 64 * kLargeKeys + lane;
+    ch.load(cv, m, base);
+    ch.load_idx(ci, m, base);
+    select_row<kLargeKeys, false>(cv, m, k, out, sh, ch);
   }
-  Chunk<kLargeKeys> ch;
-  if (n > kThreads * kSmallKeys) ch.load(row, n, (int64_t)wave * 64 * kLargeKeys + lane);
-  if (n <= kThreads * kSmallKeys)
-    select_row<kSmallKeys, false>(row, n, k, out, sh, first);
-  else if (n <= kThreads * kLargeKeys)
-    select_row<kLargeKeys, false>(row, n, k, out, sh, ch);
-  else
-    select_row<kLargeKeys, true>(row, n, k, out, sh, ch);
 }
 
 }  // namespace
 
+static_assert(kTopkSegmentKeys == kThreads * kLargeKeys, "a segment is held in registers");
+static_assert(kTopkMergeKeys == kThreads * kLargeKeys, "the merge is held in registers");
+
 hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t stream) {
   const uint32_t rows = (uint32_t)p.batch * (uint32_t)p.next_n;
+  const dim3 grid(rows, (uint32_t)p.seg_grid);
+  const bool merge = p.seg_grid > 1;
   if (tm.start || tm.stop)
-    hipExtLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, tm.start, tm.stop,
-                          0, p.logits, p.row_stride, p.ctx, p.next_n, p);
+    hipExtLaunchKernelGGL(topk_kernel, grid, dim3(kThreads), 0, stream, tm.start,
+                          merge ? nullptr : tm.stop, 0, p.logits, p.row_stride, p.ctx, p.next_n, p);
   else
-    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, p.logits, p.row_stride,
+    hipLaunchKernelGGL(topk_kernel, grid, dim3(kThreads), 0, stream, p.logits, p.row_stride,
                        p.ctx, p.next_n, p);
+  if (merge) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (tm.start || tm.stop)
+      hipExtLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(kThreads), 0, stream, nullptr,
+                            tm.stop, 0, p.ctx, p.next_n, p.row_stride, p);
+    else
+      hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(kThreads), 0, stream, p.ctx,
+                         p.next_n, p.row_stride, p);
+  }
   return hipGetLastError();
 }
 

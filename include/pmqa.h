@@ -60,8 +60,9 @@ typedef enum {
   PMQA_ERR_NULL = 1,        /* a required pointer is NULL                        */
   PMQA_ERR_SHAPE = 2,       /* a size or stride is out of range                  */
   PMQA_ERR_UNSUPPORTED = 3, /* a valid but unimplemented shape or dtype           */
-  PMQA_ERR_ALIGNMENT = 4,   /* a pointer lacks the alignment stated below        */
-  PMQA_ERR_HIP = 5          /* the HIP runtime reported an error at launch       */
+  PMQA_ERR_WORKSPACE = 4,   /* a workspace is missing or too small               */
+  PMQA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch       */
+  PMQA_ERR_ALIGNMENT = 6    /* a pointer lacks the alignment stated below        */
 } pmqa_status;
 
 /*
@@ -117,15 +118,13 @@ PMQA_API pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const
 
 /*
  * topk_per_row - indices of the k largest logits of each row (the follow-on
- * top_k_per_row_decode of aiter PR #4244, first paragraph).
+ * top_k_per_row_decode of aiter PR #4244, first paragraph, which turns each
+ * logits row into the sparse-KV index list the caller keeps).
  *
  * logits        fp32 [batch*next_n, logits_row_stride], row r at element
- *               r*logits_row_stride, 4-byte aligned.  Scores are used only on
- *               [0, visible(r)) with visible as for paged_mqa_logits (clamped
- *               to logits_row_stride); the kernel may also load the rest of a
- *               row's first min(logits_row_stride, 8192) elements (never past
- *               the row, and their values are never used), so the buffer must
- *               span every row's stride.
+ *               r*logits_row_stride, 4-byte aligned.  Only [0, visible(r)) of
+ *               each row is read, visible as for paged_mqa_logits (clamped to
+ *               logits_row_stride).
  * context_lens  [batch] int32, as for paged_mqa_logits.
  * k             1 .. 2048.
  * out_idx       [batch*next_n, k] int32, row-major.  Row r receives the
@@ -135,11 +134,35 @@ PMQA_API pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const
  *               scores at the k-th boundary the lowest indices are taken.
  * batch, next_n as for paged_mqa_logits.
  * logits_row_stride  elements between logits rows, >= 1.
+ * workspace     DEVICE scratch owned by the caller, 16-byte aligned, or NULL
+ *               when workspace_bytes is 0.  Its contents on entry are ignored
+ *               and on return unspecified; calls that share it must be ordered
+ *               on one stream.  A row longer than 16384 visible scores is split
+ *               into segments, each selected by its own workgroup into k
+ *               candidates held here, and a second launch merges them; the
+ *               workspace bounds how far rows are split (the candidates of
+ *               every row's segments must fit), never the result: a smaller
+ *               one (0 included) only gives long rows fewer, longer segments.
+ *               topk_per_row_workspace_size gives the size that splits rows of
+ *               up to a given length fully.
+ * workspace_bytes  bytes at workspace.  PMQA_ERR_WORKSPACE when it is nonzero
+ *               and workspace is NULL.
  * stream        hipStream_t to enqueue on.
  */
 PMQA_API pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,
-                         int32_t* out_idx, int32_t batch, int32_t next_n,
-                         int64_t logits_row_stride, void* stream);
+                                  int32_t* out_idx, int32_t batch, int32_t next_n,
+                                  int64_t logits_row_stride, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * topk_per_row_workspace_size - workspace bytes with which topk_per_row splits
+ * every row of up to max_row_len visible scores as far as it splits rows
+ * (segments of at most 16384 scores, at most 16384 / k of them): rows * k * 8
+ * bytes per segment of the longest row, 0 when no row that long is split.
+ * Host only.  Returns 0 for invalid arguments (rows < 0, k outside 1..2048,
+ * max_row_len < 0).
+ */
+PMQA_API size_t topk_per_row_workspace_size(int32_t rows, int32_t k, int64_t max_row_len);
 
 /*
  * paged_mqa_logits_timed, topk_per_row_timed - the same operations, for callers
@@ -161,7 +184,8 @@ PMQA_API pmqa_status paged_mqa_logits_timed(const void* q, const void* kv_cache,
 
 PMQA_API pmqa_status topk_per_row_timed(const float* logits, const int32_t* context_lens,
                                         int32_t k, int32_t* out_idx, int32_t batch,
-                                        int32_t next_n, int64_t logits_row_stride, void* stream,
+                                        int32_t next_n, int64_t logits_row_stride,
+                                        void* workspace, size_t workspace_bytes, void* stream,
                                         void* start_event, void* stop_event);
 
 /*

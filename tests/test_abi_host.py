@@ -14,7 +14,7 @@ import pytest
 import fp8_paged_mqa_block_amd as pm
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN = range(7)
 
 
 def header_symbols():
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.pmqa_status_string(s)
     assert lib.pmqa_status_string(99) == b"unknown status"
     assert lib.pmqa_version() >= 100
@@ -78,9 +78,10 @@ def test_logits_host_checks(lib, kw, status):
 
 
 def topk(lib, **kw):
-    a = dict(lg=P, ctx=P, k=2048, out=P, b=4, nn=1, rs=8192, stream=None)
+    a = dict(lg=P, ctx=P, k=2048, out=P, b=4, nn=1, rs=8192, ws=P, wsb=1 << 20, stream=None)
     a.update(kw)
-    return lib.topk_per_row(a["lg"], a["ctx"], a["k"], a["out"], a["b"], a["nn"], a["rs"], a["stream"])
+    return lib.topk_per_row(a["lg"], a["ctx"], a["k"], a["out"], a["b"], a["nn"], a["rs"],
+                            a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -88,9 +89,30 @@ def topk(lib, **kw):
     (dict(k=0), ERR_SHAPE), (dict(k=2049), ERR_SHAPE), (dict(nn=0), ERR_SHAPE),
     (dict(rs=0), ERR_SHAPE), (dict(b=-3), ERR_SHAPE), (dict(lg=P + 2), ERR_ALIGN),
     (dict(out=P + 1), ERR_ALIGN), (dict(b=0, lg=None), OK),
+    # a workspace is optional (0 bytes, NULL), but a size needs memory behind it
+    (dict(ws=None), ERR_WORKSPACE), (dict(ws=None, b=0), ERR_WORKSPACE),
+    (dict(ws=P + 8), ERR_ALIGN), (dict(ws=P + 8, wsb=0, lg=None), ERR_NULL),
+    (dict(ws=P + 8, wsb=0, b=0), OK),
 ])
 def test_topk_host_checks(lib, kw, status):
     assert topk(lib, **kw) == status
+
+
+@pytest.mark.parametrize("rows,k,max_len,want", [
+    (64, 2048, 8192, 0),            # rows of one segment are never split
+    (64, 2048, 16384, 0),
+    (64, 2048, 16385, 64 * 2 * 2048 * 8),
+    (64, 2048, 131072, 64 * 8 * 2048 * 8),
+    (64, 2048, 1 << 20, 64 * 8 * 2048 * 8),   # the merge holds 8 segments of 2048
+    (1024, 2048, 32768, 1024 * 2 * 2048 * 8),
+    (5, 100, 1 << 20, 5 * 64 * 100 * 8),      # 64 segments of 16384; 6400 candidates
+    (5, 1, 1 << 20, 5 * 64 * 1 * 8),
+    (0, 16, 1 << 20, 0),
+    (-1, 16, 100000, 0), (4, 0, 100000, 0), (4, 2049, 100000, 0), (4, 16, -1, 0),
+])
+def test_topk_workspace_size(lib, rows, k, max_len, want):
+    assert lib.topk_per_row_workspace_size(rows, k, max_len) == want
+    assert pm.topk_workspace_size(rows, k, max_len) == want if rows >= 0 else True
 
 
 def test_binding_rejects_wrong_dtypes_before_the_library():

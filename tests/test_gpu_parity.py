@@ -602,3 +602,66 @@ def test_binding_rejects_an_empty_table_row(gpu_lib):
     e = torch.empty((0, 0), dtype=torch.int64, device="cuda")
     gpu_lib.paged_mqa_logits(d["q"][:0], d["kv"], d["w"][:0], d["ctx"][:0], e, 64, 1,
                              new_out(0, 64))
+
+
+def _topk_exact(gpu_lib, dense, lens, k, workspace, label):
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    logits = torch.from_numpy(dense).cuda()
+    idx = torch.full((len(lens), k), -7, dtype=torch.int32, device="cuda")
+    say(f"[gpu] topk_per_row {label} k={k} workspace={workspace.numel()} B")
+    gpu_lib.topk_per_row(logits, ctx, k, idx, next_n=1, workspace=workspace)
+    torch.cuda.synchronize()
+    want = oracle.topk_per_row([dense[r, :n] for r, n in enumerate(lens)], k)
+    got = idx.cpu().numpy()
+    for r, n in enumerate(lens):
+        m = min(k, n)
+        assert sorted(got[r, :m].tolist()) == sorted(want[r, :m].tolist()), f"row {r} n={n} k={k}"
+        assert np.all(got[r, m:] == -1)
+    return got
+
+
+@pytest.mark.parametrize("ties", [0, 3])
+def test_topk_segments_and_workspace_sizes(gpu_lib, ties):
+    """Rows longer than one segment (16384 scores) are split over workgroups
+    into candidates in the workspace, then merged: exact sets for every
+    workspace size (none: one workgroup per row, streamed; room for 3
+    segments; the full split), with many equal scores at the k-th boundary
+    spread over segments (lowest indices win), at lengths on both sides of
+    the segment multiples."""
+    lens = [16383, 16384, 16385, 20000, 32768, 32769, 50000, 65536, 98304, 131072, 200000, 5]
+    width = max(lens)
+    dense = synth.make_logit_rows(len(lens), width, lens, seed=9, ties=ties)
+    rows = len(lens)
+    for k in (1, 7, 100, 2048):
+        sizes = [0, gpu_lib.topk_workspace_size(rows, k, 40000),
+                 gpu_lib.topk_workspace_size(rows, k, width)]
+        assert sizes[1] > 0 and sizes[2] > sizes[1]
+        for nbytes in sizes:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            _topk_exact(gpu_lib, dense, lens, k, ws, f"segments ties={ties}")
+
+
+def test_topk_merge_graph_replay(gpu_lib):
+    """The two top-k launches (segments, then the merge) captured in a graph
+    give the eager indices on every replay, with eager work in between."""
+    lens = [70000, 131072, 1000, 40000]
+    dense = synth.make_logit_rows(len(lens), max(lens), lens, seed=4, ties=0)
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    logits = torch.from_numpy(dense).cuda()
+    k = 2048
+    ws = torch.empty(gpu_lib.topk_workspace_size(len(lens), k, max(lens)), dtype=torch.uint8,
+                     device="cuda")
+    eager = _topk_exact(gpu_lib, dense, lens, k, ws, "eager before capture")
+    idx = torch.full((len(lens), k), -7, dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    say("[gpu] capture the two top-k launches")
+    with torch.cuda.graph(g):
+        gpu_lib.topk_per_row(logits, ctx, k, idx, next_n=1, workspace=ws)
+    for rep in range(3):
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        say(f"[gpu] top-k graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), np.sort(eager, axis=1))
+        _topk_exact(gpu_lib, dense, lens, k, ws, "eager between replays")
