@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pmqa_internal.h"
 #include "wave_ops.h"
 
@@ -61,6 +63,9 @@ constexpr int kSmallKeys = 8;           // keys per thread for rows up to 8192
 constexpr int kLargeKeys = 16;          // keys per thread (or per chunk) beyond
 constexpr int kCandCap = 256;           // threshold bins this small are ranked directly
 constexpr int kCandCapHeld = 128;       // the same, for rows held in registers
+// Third word of a raw buffer resource on gfx9-family chips (gfx950): 32-bit
+// elements, bounds checked against the record count in bytes.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -72,6 +77,14 @@ __device__ __forceinline__ int lane_rank(uint64_t mask) {
   // number of set bits of mask below this lane
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// v, opaque to the compiler: comparisons against it are computed where they
+// are used instead of 64-bit lane masks being kept in scalar registers across
+// a whole pass (which spills them).
+__device__ __forceinline__ int fresh(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 __device__ __forceinline__ uint32_t high_mask(int low_bits) {
@@ -99,24 +112,32 @@ struct Chunk {
   int32_t idx[IDX ? KPT : 1];
   int valid;  // keys j < valid are inside the row
 
-  __device__ __forceinline__ void load(const float* __restrict__ row, int n, int64_t base) {
-    // base = chunk start + this thread's first position; positions past the
-    // row re-read its last score (no extra cache line) and are never used
+  // The chunk at position c0 of a row of n keys (c0 < n), this thread's keys
+  // at c0 + tb + 64 j.  Buffer loads with the chunk's size as their bound:
+  // positions past the row read 0 (never used) with no per-key address
+  // arithmetic, the 64 j offsets being immediate.
+  __device__ __forceinline__ void load(const float* __restrict__ row, int n, int64_t c0, int tb) {
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(row + c0, n - c0);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int64_t i = base + 64 * j;
-      key[j] = order_key(row[i < n ? i : n - 1]);
-    }
-    set_valid(n, base);
+    for (int j = 0; j < KPT; ++j)
+      key[j] = order_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (tb + 64 * j), 0, 0)));
+    set_valid(n, c0 + tb);
   }
 
-  __device__ __forceinline__ void load_idx(const int32_t* __restrict__ ids, int n, int64_t base) {
+  __device__ __forceinline__ void load_idx(const int32_t* __restrict__ ids, int n, int64_t c0,
+                                           int tb) {
     static_assert(IDX, "a chunk without indices");
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(ids + c0, n - c0);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int64_t i = base + 64 * j;
-      idx[j] = ids[i < n ? i : n - 1];
-    }
+    for (int j = 0; j < KPT; ++j)
+      idx[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (tb + 64 * j), 0, 0);
+  }
+
+  // a raw buffer over the chunk's keys (at most kThreads * KPT of them)
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t chunk_rsrc(const void* p, int64_t left) {
+    const int64_t cnt = left < (int64_t)kThreads * KPT ? left : (int64_t)kThreads * KPT;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(4 * cnt),
+                                             kBufferFlags);
   }
 
   __device__ __forceinline__ void set_valid(int n, int64_t base) {
@@ -182,6 +203,42 @@ struct Buckets {
   }
 };
 
+// Ranks the nc keys gathered from the threshold bin (sh.cand_key, in row
+// order, with their indices in sh.cand_idx) and writes the first `remaining`
+// of them at slots first_eq + rank: larger keys first, equal keys in row
+// order (their gather order).  A candidate compares as one 64-bit value, its
+// key above its inverted position, so that one unsigned comparison orders
+// both; the slots from nc to the cap hold key 0, whose values stay below every
+// gathered key's (their positions come later).  T consecutive lanes share a
+// candidate, each comparing it with kCap / T slots, and add their counts, so
+// every wave of the workgroup takes part.
+template <int kCap, class Out>
+__device__ __forceinline__ void rank_bin_keys(TopkShared& sh, int nc, int remaining,
+                                              uint32_t first_eq, const Out& out) {
+  constexpr int T = kThreads / kCap;
+  constexpr int kPer = kCap / T;
+  static_assert(kCap * T == kThreads && kPer % 4 == 0 && (T & (T - 1)) == 0, "rank layout");
+  const int tid = threadIdx.x;
+  for (int i = nc + tid; i < kCap; i += kThreads) sh.cand_key[i] = 0u;
+  __syncthreads();
+  const int t = tid / T, part = tid % T;
+  const uint64_t mine = ((uint64_t)sh.cand_key[t] << 32) | (uint32_t)~(uint32_t)t;
+  uint32_t rank = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; u += 4) {
+    const int i = part * kPer + u;
+    const uint4 o = reinterpret_cast<const uint4*>(sh.cand_key)[i >> 2];
+    rank += ((((uint64_t)o.x << 32) | (uint32_t)~(uint32_t)i) > mine) ? 1u : 0u;
+    rank += ((((uint64_t)o.y << 32) | (uint32_t)~(uint32_t)(i + 1)) > mine) ? 1u : 0u;
+    rank += ((((uint64_t)o.z << 32) | (uint32_t)~(uint32_t)(i + 2)) > mine) ? 1u : 0u;
+    rank += ((((uint64_t)o.w << 32) | (uint32_t)~(uint32_t)(i + 3)) > mine) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int d = 1; d < T; d <<= 1) rank += (uint32_t)__shfl_xor((int)rank, d);
+  if (part == 0 && t < nc && rank < (uint32_t)remaining)
+    out.put(first_eq + rank, sh.cand_idx[t], sh.cand_key[t]);
+}
+
 // Selects the row's top k; `ch` holds the row's first chunk (already loaded).
 //
 // Keys are narrowed in passes until the bin holding the k-th largest key is
@@ -201,7 +258,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   const int wave = tid >> 6;
   constexpr int kChunk = kThreads * KPT;
   const int n_chunks = STREAM ? (n + kChunk - 1) / kChunk : 1;
-  const int64_t thread_base = (int64_t)wave * 64 * KPT + lane;
+  const int thread_base = wave * 64 * KPT + lane;
 
   // Runs body(chunk, c) over the row's chunks in order; `ch` holds chunk 0 on
   // entry.  A streamed row alternates two register chunks so that the next
@@ -213,24 +270,25 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
       body(ch, 0);
     } else {
       for (int c = 0; c < n_chunks; c += 2) {
-        if (c + 1 < n_chunks) nx.load(row, n, (int64_t)(c + 1) * kChunk + thread_base);
+        if (c + 1 < n_chunks) nx.load(row, n, (int64_t)(c + 1) * kChunk, thread_base);
         body(ch, c);
-        if (c + 2 < n_chunks) ch.load(row, n, (int64_t)(c + 2) * kChunk + thread_base);
+        if (c + 2 < n_chunks) ch.load(row, n, (int64_t)(c + 2) * kChunk, thread_base);
         if (c + 1 < n_chunks) body(nx, c + 1);
       }
     }
   };
   // a streamed row's later passes start again from chunk 0
   auto rewind = [&]() {
-    if constexpr (STREAM) ch.load(row, n, thread_base);
+    if constexpr (STREAM) ch.load(row, n, 0, thread_base);
   };
 
   // ---- the row's largest and smallest key ----
   uint32_t kmax = 0u, kmin = ~0u;
   for_chunks([&](const Chunk<KPT, IDX>& cc, int) {
+    const int vld = fresh(cc.valid);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      if (j < cc.valid) {
+      if (j < vld) {
         kmax = max(kmax, cc.key[j]);
         kmin = min(kmin, cc.key[j]);
       }
@@ -251,6 +309,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   int bits_left = kmax == kmin ? 0 : 32 - __builtin_clz(kmax ^ kmin);
   uint32_t mask = high_mask(bits_left);
   uint32_t prefix = kmax & mask;
+  const uint32_t mask0 = mask;
   int remaining = k;  // rank of the k-th key among the keys in the threshold bin
   bool whole_bin = false;
   int buf = 0;
@@ -272,12 +331,13 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
     uint32_t* h = sh.hist[buf];
     rewind();
     for_chunks([&](const Chunk<KPT, IDX>& cc, int) {
+      const int vld = fresh(cc.valid);
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const uint32_t key = cc.key[j];
         if (bucket_pass) {
-          if (j < cc.valid) atomicAdd(&h[kb[j]], 1u);
-        } else if (j < cc.valid && kb[j] == bstar && (key & mask) == prefix) {
+          if (j < vld) atomicAdd(&h[kb[j]], 1u);
+        } else if (j < vld && kb[j] == bstar && (key & mask) == prefix) {
           atomicAdd(&h[(key >> shift) & dmask], 1u);
         }
       }
@@ -348,95 +408,78 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row, int n,
   // threshold bin take slots k - remaining + rank while rank < remaining:
   // rank in row order when the bin is taken whole or its keys are equal;
   // otherwise the bin's keys are first gathered (in row order) and each one's
-  // rank among them computed below
+  // rank among them computed below.  When the value buckets resolved the
+  // threshold (no radix digit fixed after them) every key shares the fixed
+  // bits, so a key's bucket alone classifies it.
   const uint32_t first_eq = (uint32_t)(k - remaining);
+  const bool by_bucket = bk.on && mask == mask0;
   uint32_t run_a = 0, run_e = 0;
-  rewind();
-  for_chunks([&](const Chunk<KPT, IDX>& cc, int c) {
-    bool is_a[KPT], is_e[KPT];
-    uint32_t ca = 0, ce = 0;
+  auto write_pass = [&](auto fast) {
+    // class of key j: above the threshold bin, or in it
+    auto above = [&](const Chunk<KPT, IDX>& cc, int j, uint32_t bs, uint32_t m, uint32_t pf) {
+      if constexpr (decltype(fast)::value) return kb[j] > bs;
+      else return kb[j] > bs || (kb[j] == bs && (cc.key[j] & m) > pf);
+    };
+    auto inbin = [&](const Chunk<KPT, IDX>& cc, int j, uint32_t bs, uint32_t m, uint32_t pf) {
+      if constexpr (decltype(fast)::value) return kb[j] == bs;
+      else return kb[j] == bs && (cc.key[j] & m) == pf;
+    };
+    rewind();
+    for_chunks([&](const Chunk<KPT, IDX>& cc, int c) {
+      uint32_t ca = 0, ce = 0;
+      const int vld = fresh(cc.valid);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint32_t kp = cc.key[j] & mask;
-      const bool ok = j < cc.valid;
-      is_a[j] = ok && (kb[j] > bstar || (kb[j] == bstar && kp > prefix));
-      is_e[j] = ok && kb[j] == bstar && kp == prefix;
-      ca += (uint32_t)__popcll(__ballot(is_a[j]));
-      ce += (uint32_t)__popcll(__ballot(is_e[j]));
-    }
-    if (lane == 0) {
-      sh.col_a[c & 1][wave] = ca;
-      sh.col_e[c & 1][wave] = ce;
-    }
-    __syncthreads();
-    const uint32_t pa = row_prefix(sh.col_a[c & 1][lane & 15]);
-    const uint32_t pe = row_prefix(sh.col_e[c & 1][lane & 15]);
-    const uint32_t ta = lane_of(pa, 15), te = lane_of(pe, 15);
-    uint32_t off_a = run_a + lane_of(pa, wave) - ca;  // exclusive over waves
-    uint32_t off_e = run_e + lane_of(pe, wave) - ce;
-    const int64_t base = (int64_t)c * kChunk + thread_base;
-    // the flags pass through an empty asm statement so that the ballots below
-    // are taken again instead of keeping the first loop's 2 * KPT masks live
-    // in scalar registers across the barrier
-    int fa[KPT], fe[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      fa[j] = is_a[j];
-      fe[j] = is_e[j];
-      asm volatile("" : "+v"(fa[j]), "+v"(fe[j]));
-    }
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint64_t ma = __ballot(fa[j] != 0);
-      const uint64_t me = __ballot(fe[j] != 0);
-      const int32_t idx = cc.index(j, base + 64 * j);
-      if (fa[j]) out.put(off_a + (uint32_t)lane_rank(ma), idx, cc.key[j]);
-      if (fe[j]) {
-        const uint32_t rank = off_e + (uint32_t)lane_rank(me);
-        if (rank_bin) {
-          sh.cand_key[rank] = cc.key[j];
-          sh.cand_idx[rank] = idx;
-        } else if (rank < (uint32_t)remaining) {
-          out.put(first_eq + rank, idx, cc.key[j]);
-        }
+      for (int j = 0; j < KPT; ++j) {
+        const bool ok = j < vld;
+        ca += (uint32_t)__popcll(__ballot(ok && above(cc, j, bstar, mask, prefix)));
+        ce += (uint32_t)__popcll(__ballot(ok && inbin(cc, j, bstar, mask, prefix)));
       }
-      off_a += (uint32_t)__popcll(ma);
-      off_e += (uint32_t)__popcll(me);
-    }
-    run_a += ta;
-    run_e += te;
-  });
+      if (lane == 0) {
+        sh.col_a[c & 1][wave] = ca;
+        sh.col_e[c & 1][wave] = ce;
+      }
+      __syncthreads();
+      const uint32_t pa = row_prefix(sh.col_a[c & 1][lane & 15]);
+      const uint32_t pe = row_prefix(sh.col_e[c & 1][lane & 15]);
+      const uint32_t ta = lane_of(pa, 15), te = lane_of(pe, 15);
+      uint32_t off_a = run_a + lane_of(pa, wave) - ca;  // exclusive over waves
+      uint32_t off_e = run_e + lane_of(pe, wave) - ce;
+      const int64_t base = (int64_t)c * kChunk + thread_base;
+      // the threshold passes through an empty asm statement, so that the
+      // classes below are computed again instead of the first loop's 2 * KPT
+      // ballots being kept live across the barrier
+      uint32_t bs = bstar, m = mask, pf = prefix;
+      asm volatile("" : "+v"(bs), "+v"(m), "+v"(pf));
+      const int vld2 = fresh(cc.valid);
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool ok = j < vld2;
+        const bool fa = ok && above(cc, j, bs, m, pf);
+        const bool fe = ok && inbin(cc, j, bs, m, pf);
+        const uint64_t ma = __ballot(fa);
+        const uint64_t me = __ballot(fe);
+        const int32_t idx = cc.index(j, base + 64 * j);
+        if (fa) out.put(off_a + (uint32_t)lane_rank(ma), idx, cc.key[j]);
+        if (fe) {
+          const uint32_t rank = off_e + (uint32_t)lane_rank(me);
+          if (rank_bin) {
+            sh.cand_key[rank] = cc.key[j];
+            sh.cand_idx[rank] = idx;
+          } else if (rank < (uint32_t)remaining) {
+            out.put(first_eq + rank, idx, cc.key[j]);
+          }
+        }
+        off_a += (uint32_t)__popcll(ma);
+        off_e += (uint32_t)__popcll(me);
+      }
+      run_a += ta;
+      run_e += te;
+    });
+  };
+  if (by_bucket) write_pass(std::true_type{});
+  else write_pass(std::false_type{});
   if (!rank_bin) return;
-  // rank of each gathered key among the bin's nc keys: larger keys first,
-  // equal keys in row order (their gather order).  A candidate compares as one
-  // 64-bit value, its key above its inverted position, so that one unsigned
-  // comparison orders both; the slots from nc to the cap hold key 0, whose
-  // values stay below every gathered key's (their positions come later).
-  // T consecutive lanes share a candidate, each comparing it with kCap / T
-  // slots, and add their counts, so every wave of the workgroup takes part.
-  constexpr int kCap = STREAM ? kCandCap : kCandCapHeld;
-  constexpr int T = kThreads / kCap;
-  constexpr int kPer = kCap / T;
-  static_assert(kCap * T == kThreads && kPer % 4 == 0 && (T & (T - 1)) == 0, "rank layout");
-  const int nc = (int)run_e;
-  for (int i = nc + tid; i < kCap; i += kThreads) sh.cand_key[i] = 0u;
-  __syncthreads();
-  const int t = tid / T, part = tid % T;
-  const uint64_t mine = ((uint64_t)sh.cand_key[t] << 32) | (uint32_t)~(uint32_t)t;
-  uint32_t rank = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; u += 4) {
-    const int i = part * kPer + u;
-    const uint4 o = reinterpret_cast<const uint4*>(sh.cand_key)[i >> 2];
-    rank += ((((uint64_t)o.x << 32) | (uint32_t)~(uint32_t)i) > mine) ? 1u : 0u;
-    rank += ((((uint64_t)o.y << 32) | (uint32_t)~(uint32_t)(i + 1)) > mine) ? 1u : 0u;
-    rank += ((((uint64_t)o.z << 32) | (uint32_t)~(uint32_t)(i + 2)) > mine) ? 1u : 0u;
-    rank += ((((uint64_t)o.w << 32) | (uint32_t)~(uint32_t)(i + 3)) > mine) ? 1u : 0u;
-  }
-#pragma unroll
-  for (int d = 1; d < T; d <<= 1) rank += (uint32_t)__shfl_xor((int)rank, d);
-  if (part == 0 && t < nc && rank < (uint32_t)remaining)
-    out.put(first_eq + rank, sh.cand_idx[t], sh.cand_key[t]);
+  rank_bin_keys<STREAM ? kCandCap : kCandCapHeld>(sh, (int)run_e, remaining, first_eq, out);
 }
 
 // Visible scores of row r (a row never reads past its stride).
@@ -449,42 +492,41 @@ __device__ __forceinline__ int row_len(const int32_t* __restrict__ ctx_lens, int
   return (int64_t)n > row_stride ? (int)row_stride : n;
 }
 
-// Segments of a row of n > k scores: one per kTopkSegmentKeys scores, at most
-// `grid` (the launch's second dimension, which the host bounds by the
-// workspace and by the merge's capacity).
-__device__ __forceinline__ int row_segments(int n, int grid) {
-  return min((n + kTopkSegmentKeys - 1) / kTopkSegmentKeys, grid);
-}
-
 // Selects n keys at `row` (positions 0..n-1) into `out`, with the register
-// layout their count calls for.
+// layout their count calls for.  Without STREAM the caller guarantees n <=
+// kTopkSegmentKeys (the keys fit the registers).
+template <bool STREAM>
 __device__ __forceinline__ void select_keys(const float* __restrict__ row, int n, int k,
                                             const SelectOut& out, TopkShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (n <= kThreads * kSmallKeys) {
     Chunk<kSmallKeys> ch;
-    ch.load(row, n, (int64_t)wave * 64 * kSmallKeys + lane);
+    ch.load(row, n, 0, wave * 64 * kSmallKeys + lane);
     select_row<kSmallKeys, false>(row, n, k, out, sh, ch);
+  } else if (!STREAM || n <= kThreads * kLargeKeys) {
+    Chunk<kLargeKeys> ch;
+    ch.load(row, n, 0, wave * 64 * kLargeKeys + lane);
+    select_row<kLargeKeys, false>(row, n, k, out, sh, ch);
   } else {
     Chunk<kLargeKeys> ch;
-    ch.load(row, n, (int64_t)wave * 64 * kLargeKeys + lane);
-    if (n <= kThreads * kLargeKeys) select_row<kLargeKeys, false>(row, n, k, out, sh, ch);
-    else select_row<kLargeKeys, true>(row, n, k, out, sh, ch);
+    ch.load(row, n, 0, wave * 64 * kLargeKeys + lane);
+    select_row<kLargeKeys, true>(row, n, k, out, sh, ch);
   }
 }
 
 // Stage 1.  Workgroup (r, s) selects segment s of row r: the whole row when
 // it has one segment (the result goes straight to out_idx), otherwise k
-// candidates of the segment into the workspace.  The row pointer, stride,
-// context lengths and next_n come first as scalar arguments: the dispatch
-// preloads them into SGPRs (the build asks for up to 16 preloaded dwords), so
-// the context-length load issues at once.
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ logits,
-                                                       int64_t row_stride,
-                                                       const int32_t* __restrict__ ctx_lens,
-                                                       int32_t next_n, TopkParams p) {
-  __shared__ TopkShared sh;
-
+// candidates of the segment into the workspace.  Segments hold at most
+// kTopkSegmentKeys keys, except that STREAM (a grid of one segment per row,
+// the workspace too small to split anything, on rows the stride allows to be
+// longer) selects any row whole, streaming it through the registers.  With
+// more than one segment per row, a row that would need more segments than
+// the grid has is left to the merge launch, which selects it whole, so the
+// stage keeps only the register-resident layouts.
+template <bool STREAM>
+__device__ __forceinline__ void stage1(const float* __restrict__ logits, int64_t row_stride,
+                                       const int32_t* __restrict__ ctx_lens, int32_t next_n,
+                                       const TopkParams& p, TopkShared& sh) {
   const int r = blockIdx.x;
   const int s = blockIdx.y;
   const int n = row_len(ctx_lens, r, next_n, row_stride);
@@ -495,7 +537,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const int nseg = row_segments(n, (int)gridDim.y);
+  const int need = (n + kTopkSegmentKeys - 1) / kTopkSegmentKeys;
+  const int grid = (int)gridDim.y;
+  if (grid > 1 && need > grid) return;  // selected whole by the merge launch
+  const int nseg = min(need, grid);
   if (s >= nseg) return;
   // a row of one segment selects straight into out_idx; otherwise nearly
   // equal segments (each holds more than k scores: at least half a segment's
@@ -504,13 +549,42 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const int64_t slot = ((int64_t)r * gridDim.y + s) * k;
   const SelectOut so = nseg == 1 ? SelectOut{out, nullptr, 0}
                                  : SelectOut{p.cand_idx + slot, p.cand_val + slot, (int32_t)s0};
-  select_keys(logits + (int64_t)r * row_stride + s0, (int)(s1 - s0), k, so, sh);
+  select_keys<STREAM>(logits + (int64_t)r * row_stride + s0, (int)(s1 - s0), k, so, sh);
 }
 
-// Stage 2.  Workgroup r selects the top k of row r among its segments'
-// nseg * k candidates (at most kTopkMergeKeys: the host caps the segments),
-// held in registers with their indices.  Rows of one segment or none were
-// finished in stage 1.
+// Stage 1 for grids of one segment per row.  The row pointer, stride, context
+// lengths and next_n come first as scalar arguments: the dispatch preloads
+// them into SGPRs (the build asks for up to 16 preloaded dwords), so the
+// context-length load issues at once.
+template <bool STREAM>
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ logits,
+                                                       int64_t row_stride,
+                                                       const int32_t* __restrict__ ctx_lens,
+                                                       int32_t next_n, TopkParams p) {
+  __shared__ TopkShared sh;
+  stage1<STREAM>(logits, row_stride, ctx_lens, next_n, p, sh);
+}
+
+// Stage 1 for grids that split rows: many workgroups, so two should share a
+// CU.  The register-resident select needs 52 VGPRs (eight waves per SIMD fit)
+// but about 93 SGPRs, and on gfx950 a second 1024-thread workgroup then does
+// not fit a CU (measured: one workgroup per CU at 93-97 SGPRs, two at 80 and
+// below), so the compiler is held to 80 SGPRs (it moves the rest to VGPR
+// lanes).  Measured on the MTP, small-pages and long-context workloads: 15%
+// less time than one workgroup per CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
+void topk_split_kernel(const float* __restrict__ logits, int64_t row_stride,
+                       const int32_t* __restrict__ ctx_lens, int32_t next_n, TopkParams p) {
+  __shared__ TopkShared sh;
+  stage1<false>(logits, row_stride, ctx_lens, next_n, p, sh);
+}
+
+// Stage 2 (launched when the grid has more than one segment per row).
+// Workgroup r selects the top k of row r among its segments' nseg * k
+// candidates (at most kTopkMergeKeys: the host caps the segments), held in
+// registers with their indices; or, for a row longer than the grid's
+// segments can hold, the whole row, streamed.  Rows of one segment or none
+// were finished in stage 1.
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __restrict__ ctx_lens,
                                                              int32_t next_n, int64_t row_stride,
                                                              TopkParams p) {
@@ -520,25 +594,30 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __r
   const int n = row_len(ctx_lens, r, next_n, row_stride);
   const int k = p.k;
   if (n <= k) return;
-  const int nseg = row_segments(n, p.seg_grid);
+  const int need = (n + kTopkSegmentKeys - 1) / kTopkSegmentKeys;
+  const SelectOut out{p.out_idx + (int64_t)r * k, nullptr, 0};
+  if (need > p.seg_grid) {
+    select_keys<true>(p.logits + (int64_t)r * row_stride, n, k, out, sh);
+    return;
+  }
+  const int nseg = need;
   if (nseg < 2) return;
   const int m = nseg * k;
   const int64_t slot = (int64_t)r * p.seg_grid * k;
   const float* cv = p.cand_val + slot;
   const int32_t* ci = p.cand_idx + slot;
-  const SelectOut out{p.out_idx + (int64_t)r * k, nullptr, 0};
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (m <= kThreads * kSmallKeys) {
     Chunk<kSmallKeys, true> ch;
-    const int64_t base = (int64_t)wave * 64 * kSmallKeys + lane;
-    ch.load(cv, m, base);
-    ch.load_idx(ci, m, base);
+    const int tb = wave * 64 * kSmallKeys + lane;
+    ch.load(cv, m, 0, tb);
+    ch.load_idx(ci, m, 0, tb);
     select_row<kSmallKeys, false>(cv, m, k, out, sh, ch);
   } else {
     Chunk<kLargeKeys, true> ch;
-    const int64_t base = (int64_t)wave * 64 * kLargeKeys + lane;
-    ch.load(cv, m, base);
-    ch.load_idx(ci, m, base);
+    const int tb = wave * 64 * kLargeKeys + lane;
+    ch.load(cv, m, 0, tb);
+    ch.load_idx(ci, m, 0, tb);
     select_row<kLargeKeys, false>(cv, m, k, out, sh, ch);
   }
 }
@@ -552,12 +631,18 @@ hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t 
   const uint32_t rows = (uint32_t)p.batch * (uint32_t)p.next_n;
   const dim3 grid(rows, (uint32_t)p.seg_grid);
   const bool merge = p.seg_grid > 1;
+  // with one segment per row, rows longer than the registers hold are
+  // streamed by stage 1 itself (when the stride allows such rows); with more,
+  // the merge launch takes them
+  const int64_t longest = p.row_stride < INT32_MAX ? p.row_stride : INT32_MAX;
+  const bool stream_keys = !merge && longest > kTopkSegmentKeys;
+  auto kern = merge ? topk_split_kernel : (stream_keys ? topk_kernel<true> : topk_kernel<false>);
   if (tm.start || tm.stop)
-    hipExtLaunchKernelGGL(topk_kernel, grid, dim3(kThreads), 0, stream, tm.start,
+    hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, tm.start,
                           merge ? nullptr : tm.stop, 0, p.logits, p.row_stride, p.ctx, p.next_n, p);
   else
-    hipLaunchKernelGGL(topk_kernel, grid, dim3(kThreads), 0, stream, p.logits, p.row_stride,
-                       p.ctx, p.next_n, p);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, p.logits, p.row_stride, p.ctx,
+                       p.next_n, p);
   if (merge) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
