@@ -33,7 +33,8 @@ _lib: Optional[ctypes.CDLL] = None
 
 # Every symbol include/pmqa.h declares.
 EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "topk_per_row", "topk_per_row_timed",
-           "topk_per_row_workspace_size", "pmqa_check_inputs", "quantize_k_cache",
+           "topk_per_row_workspace_size", "topk_per_row_noalloc", "pmqa_check_inputs",
+           "quantize_k_cache",
            "quantize_k_cache_timed", "pmqa_status_string", "pmqa_version", "pmqa_logits_kernel")
 
 # pmqa_dtype codes of the K rows quantize_k_cache accepts
@@ -83,6 +84,8 @@ def load_library() -> ctypes.CDLL:
     lib.topk_per_row.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp, ctypes.c_size_t, vp]
     lib.topk_per_row_timed.restype = ctypes.c_int
     lib.topk_per_row_timed.argtypes = lib.topk_per_row.argtypes + [vp, vp]
+    lib.topk_per_row_noalloc.restype = ctypes.c_int
+    lib.topk_per_row_noalloc.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp]
     lib.topk_per_row_workspace_size.restype = ctypes.c_size_t
     lib.topk_per_row_workspace_size.argtypes = [c_i32, c_i32, c_i64]
     lib.pmqa_check_inputs.restype = ctypes.c_int

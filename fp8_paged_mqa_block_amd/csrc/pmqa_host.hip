@@ -286,6 +286,27 @@ pmqa_status topk_per_row_timed(const float* logits, const int32_t* context_lens,
                    workspace_bytes, stream, timing(start_event, stop_event));
 }
 
+static_assert(PMQA_NOALLOC_SCRATCH_BYTES == pmqa::kTopkScratchBytes,
+              "the header states the scratch size the library holds");
+
+pmqa_status topk_per_row_noalloc(const float* logits, const int32_t* context_lens, int32_t k,
+                                 int32_t* out_idx, int32_t batch, int32_t next_n,
+                                 int64_t logits_row_stride, void* stream) {
+  // the split topk_per_row makes for rows as long as the stride, in the
+  // library's fixed scratch; larger is refused before anything else happens
+  if (batch < 0 || next_n < 1 || logits_row_stride < 1) return PMQA_ERR_SHAPE;
+  if (k < 1 || k > 2048) return PMQA_ERR_SHAPE;
+  if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
+  const size_t need = topk_per_row_workspace_size(batch * next_n, k, logits_row_stride);
+  if (need > pmqa::kTopkScratchBytes) return PMQA_ERR_WORKSPACE;
+  if (batch == 0) return PMQA_OK;
+  if (!logits || !context_lens || !out_idx) return PMQA_ERR_NULL;
+  void* scratch = nullptr;
+  if (need > 0 && pmqa::topk_scratch(&scratch) != hipSuccess) return PMQA_ERR_HIP;
+  return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, scratch,
+                   need, stream, pmqa::LaunchTiming{});
+}
+
 size_t topk_per_row_workspace_size(int32_t rows, int32_t k, int64_t max_row_len) {
   if (rows < 0 || k < 1 || k > 2048 || max_row_len < 0) return 0;
   const int64_t g = pmqa::topk_segment_grid(rows, k, max_row_len, UINT64_MAX);

@@ -79,6 +79,12 @@ struct TopkParams {
   int32_t seg_grid;        // most segments a row is split into (1: no split)
 };
 
+// Bytes of the fixed scratch array the allocation-free top-k uses as its
+// workspace (one copy per GPU).
+constexpr uint64_t kTopkScratchBytes = uint64_t{32} << 20;
+// This device's copy of that array (looked up once per device).
+hipError_t topk_scratch(void** ptr);
+
 // Most segments a row of up to max_row_len scores is split into, given the
 // workspace bytes for its candidates (0 bytes: 1, no split).
 int64_t topk_segment_grid(int64_t rows, int32_t k, int64_t max_row_len, uint64_t workspace_bytes);

@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pmqa_internal.h"
@@ -626,6 +627,33 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __r
 
 static_assert(kTopkSegmentKeys == kThreads * kLargeKeys, "a segment is held in registers");
 static_assert(kTopkMergeKeys == kThreads * kLargeKeys, "the merge is held in registers");
+
+// Scratch of the allocation-free top-k: the candidates of split rows, in a
+// fixed device array (one copy per GPU, held until the process ends), for
+// callers that cannot allocate.  Calls on one GPU share it; nothing in it has
+// to start at zero (a call writes every candidate it reads).
+static __device__ __align__(256) uint8_t scratch[kTopkScratchBytes];
+
+hipError_t topk_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // the array's name is a host-side stand-in: its device address (this
+    // device's copy) comes from the runtime, once per device
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t stream) {
   const uint32_t rows = (uint32_t)p.batch * (uint32_t)p.next_n;

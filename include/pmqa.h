@@ -155,6 +155,30 @@ PMQA_API pmqa_status topk_per_row(const float* logits, const int32_t* context_le
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * topk_per_row_noalloc - topk_per_row for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, checks and results as topk_per_row,
+ * without the workspace: the candidates of split rows go to a scratch array
+ * the library holds in device memory, PMQA_NOALLOC_SCRATCH_BYTES per GPU
+ * (allocated with the library's code on each GPU it runs on, kept until the
+ * process ends).  Rows are split exactly as topk_per_row splits them with a
+ * workspace of topk_per_row_workspace_size(batch*next_n, k, logits_row_stride)
+ * bytes; when that exceeds PMQA_NOALLOC_SCRATCH_BYTES the call returns
+ * PMQA_ERR_WORKSPACE and enqueues nothing.  It calls no allocating routine.
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap
+ * on a GPU (different streams, different threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe.  Nothing in
+ * the scratch has to start at zero (each call writes what it reads).  The
+ * first call on a device looks up that device's copy (hipGetSymbolAddress);
+ * a failure there returns PMQA_ERR_HIP.
+ */
+#define PMQA_NOALLOC_SCRATCH_BYTES (32u << 20)
+PMQA_API pmqa_status topk_per_row_noalloc(const float* logits, const int32_t* context_lens,
+                                          int32_t k, int32_t* out_idx, int32_t batch,
+                                          int32_t next_n, int64_t logits_row_stride,
+                                          void* stream);
+
+/*
  * topk_per_row_workspace_size - workspace bytes with which topk_per_row splits
  * every row of up to max_row_len visible scores as far as it splits rows
  * (segments of at most 16384 scores, at most 16384 / k of them): rows * k * 8

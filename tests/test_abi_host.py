@@ -192,3 +192,31 @@ def test_logits_kernel_name_errors(lib):
     big = ctypes.create_string_buffer(64)
     assert lib.pmqa_logits_kernel(2, 1, 64, 1024, 96, 128, 16, big, 64) == ERR_UNSUPPORTED
     assert lib.pmqa_logits_kernel(2, 1, 48, 1024, 64, 128, 16, big, 64) == ERR_SHAPE
+
+
+def noalloc(lib, **kw):
+    a = dict(lg=P, ctx=P, k=2048, out=P, b=64, nn=1, rs=131072, stream=None)
+    a.update(kw)
+    return lib.topk_per_row_noalloc(a["lg"], a["ctx"], a["k"], a["out"], a["b"], a["nn"], a["rs"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lg=None), ERR_NULL), (dict(ctx=None), ERR_NULL), (dict(out=None), ERR_NULL),
+    (dict(k=0), ERR_SHAPE), (dict(nn=0), ERR_SHAPE), (dict(rs=0), ERR_SHAPE), (dict(b=-1), ERR_SHAPE),
+    # the split the stride calls for needs more than the library's scratch:
+    # 1024 rows * 8 segments * 2048 candidates * 8 bytes = 128 MiB > 32 MiB
+    (dict(b=1024, rs=1 << 20), ERR_WORKSPACE), (dict(b=1024, rs=1 << 20, lg=None), ERR_WORKSPACE),
+    (dict(b=0), OK), (dict(b=0, lg=None), OK),
+])
+def test_topk_noalloc_host_checks(lib, kw, status):
+    assert noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_size_in_header_matches_a_full_split():
+    text = open(os.path.join(ROOT, "include", "pmqa.h")).read()
+    m = re.search(r"#define PMQA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == 32 << 20
+    # the long-context workload's full split fits; the MTP workload's stride does not
+    assert pm.topk_workspace_size(64, 2048, 131072) <= 32 << 20
+    assert pm.topk_workspace_size(1024, 2048, 1 << 20) > 32 << 20
