@@ -41,7 +41,7 @@ FP8_PEAK_TFLOPS = 5000.0
 N_SETS = 16
 KERNEL_SOURCES = ["fp8_paged_mqa_block_amd/csrc/logits_gfx950.hip",
                   "fp8_paged_mqa_block_amd/csrc/pmqa_host.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "logits_decode_b64_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_traffic.md")
 
 
 class HipEvents:
@@ -402,6 +402,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the step (no copy, token-level or producer measurements): "
                          "for profiler runs whose per-kernel figures must cover the step alone")
+    ap.add_argument("--table", choices=("permuted", "identity"), default="permuted",
+                    help="page order of the workload's pool (identity: each request's pages "
+                         "contiguous, for comparison with the permuted pool)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip timing the other workloads")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -424,7 +427,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
-    wl = synth.make_config(args.config)
+    wl = synth.make_config(args.config, table=args.table)
     rows, stride, k = wl.rows, wl.out_row_stride, wl.topk
     print(f"[bench] workload {wl.name}: B={wl.batch} next_n={wl.next_n} H={wl.heads} "
           f"ps={wl.page_size} scored={wl.scored_tokens()} sets={args.sets}", file=sys.stderr,
@@ -533,7 +536,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.batch, "next_n": wl.next_n,
+        "config": {"workload": wl.name, "page_order": args.table, "batch": wl.batch, "next_n": wl.next_n,
                    "heads": wl.heads, "head_dim": wl.head_dim, "page_size": wl.page_size,
                    "context_lens": "U[1,8192]" if args.config == 2 else "see workload",
                    "topk": k, "scored_tokens_per_step": scored, "rotated_input_sets": args.sets,

@@ -81,6 +81,15 @@ constexpr int kMaxPages = kIterTokens;                    // page ids per iterat
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// Cache policy of the K gather: non-temporal (the NT bit of gfx950's load
+// cache-policy field).  Every K record is read once per launch, so marking its
+// lines as streaming keeps them from displacing what is reused from L2 (block
+// table, q, weights).  Measured on the decode workload (interleaved with the
+// default policy in one process): 10.56 -> 9.80 us mean per launch; the same
+// on a pool whose pages are contiguous (10.42 -> 9.84 us), which also shows
+// the page scatter itself costs nothing measurable.
+constexpr int kStreamK = 2;
+
 // A lane's 32 bytes of one 128-byte q row or K record as an MFMA operand:
 // the 16 bytes at p and the 16 at p + 64 (p = row + 16*kq).  The matrix
 // core's K order only has to agree between q and K; this one reads each row
@@ -499,7 +508,7 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
     const uint8_t* src = p.kv + base;
 #pragma unroll
     for (int i = 0; i < kGatherLoads; ++i)
-      __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, kStreamK);
     return;
   }
   // Pages here hold at most 32 tokens and the iteration starts at a multiple
@@ -525,7 +534,7 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
   for (int i = 0; i < kGatherLoads; ++i) {
     const int64_t off = t0 + (int)rec[i] < limit ? (int64_t)((uint64_t)pg.id[i] * pb + in_page[i])
                                                  : (int64_t)(16 * (lane & 7));
-    __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * kDmaBytes), 16, 0, kStreamK);
   }
 }
 
@@ -539,7 +548,7 @@ __device__ __forceinline__ void gather_page(const LogitsParams& p, int it, int64
       p.kv + id * p.page_bytes + (int32_t)((t0 & (p.page_size - 1)) * kRecordBytes);
 #pragma unroll
   for (int i = 0; i < kGatherLoads; ++i)
-    __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, kStreamK);
 }
 
 // The page id of an iteration that lies in one page, by a scalar load (the

@@ -274,7 +274,11 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(cfg: int, seed: int = 0) -> Workload:
+def make_config(cfg: int, seed: int = 0, table: str = "permuted") -> Workload:
+    """Workload `cfg` (1-5).  `table` = "identity" lays each request's pages out
+    contiguously in the same pool (workloads 2-5; the first is identity
+    already), for comparing a scattered page stream with a contiguous one."""
+    assert table in ("permuted", "identity")
     if cfg == 1:
         # B=2, next_n=1, H=64, D=128, 64-token pages, ctx [1000, 1024], identity table
         return build_workload(
@@ -286,14 +290,14 @@ def make_config(cfg: int, seed: int = 0) -> Workload:
         # B=64 decode, ctx U[1,8192], permuted table over a 10,000-page pool
         return build_workload(
             "decode_b64", batch=64, next_n=1, heads=64, head_dim=128, page_size=64,
-            ctx_range=(1, 8192), table="permuted", pool_pages=10_000, table_width=128,
+            ctx_range=(1, 8192), table=table, pool_pages=10_000, table_width=128,
             topk=2048, out_row_stride=8192, seed=seed,
         )
     if cfg == 3:
         # B=256, next_n=4 (1024 rows), H=128, 256-token pages, out [1024, 1<<20]
         return build_workload(
             "mtp_wide_output", batch=256, next_n=4, heads=128, head_dim=128, page_size=256,
-            ctx_range=(2, 32768), table="permuted", pool_pages=40_960, table_width=128,
+            ctx_range=(2, 32768), table=table, pool_pages=40_960, table_width=128,
             topk=2048, out_row_stride=1 << 20, seed=seed,
         )
     if cfg == 4:
@@ -301,7 +305,7 @@ def make_config(cfg: int, seed: int = 0) -> Workload:
         # a 2^21-page pool so that used pages sit past 2^31 bytes
         return build_workload(
             "small_pages", batch=128, next_n=3, heads=64, head_dim=128, page_size=8,
-            ctx_range=(0, 65536), table="permuted", pool_pages=1 << 21, table_width=8192,
+            ctx_range=(0, 65536), table=table, pool_pages=1 << 21, table_width=8192,
             zero_every=16, ctx_fixups={1: 1, 2: 7, 3: 8, 4: 9, 5: 65536},
             topk=2048, out_row_stride=65536, seed=seed, padded_width=16384,
         )
@@ -309,7 +313,7 @@ def make_config(cfg: int, seed: int = 0) -> Workload:
         # B=32, next_n=2, H=128, ctx U[65536,131072], log-normal per-token scales
         return build_workload(
             "long_context", batch=32, next_n=2, heads=128, head_dim=128, page_size=64,
-            ctx_range=(65536, 131072), table="permuted", pool_pages=1 << 17, table_width=2048,
+            ctx_range=(65536, 131072), table=table, pool_pages=1 << 17, table_width=2048,
             lognormal_scales=True, topk=2048, out_row_stride=131072, seed=seed,
         )
     raise ValueError(f"unknown config {cfg}")
