@@ -15,7 +15,10 @@ What it computes (the plain definition, written out):
   with -1 when a row sees fewer than k tokens;
 * the K-cache records the logits read, produced from new K rows (per-token
   scale amax/448, e4m3fn codes by round-to-nearest-even, records written at
-  int64 slots): ``oracle.k_cache``.
+  int64 slots): ``oracle.k_cache``;
+* the preshuffled page layout (a format of this path: tiles of min(page, 16)
+  tokens whose operand pieces are contiguous): ``oracle.layout``, read by the
+  gather and written by the K-cache writer.
 
 Sources: the op and its tensors are those of ``deepgemm_fp8_paged_mqa_logits``
 (aiter PR #4244 "fix silent tail-row drop in deepgemm_fp8_paged_mqa_logits at
@@ -42,6 +45,7 @@ from .paged_mqa import (  # noqa: F401
     topk_per_row,
     NEG_INF_BITS,
 )
+from .layout import preshuffled_offsets, tile_rows  # noqa: F401,E402
 from .k_cache import (  # noqa: F401,E402
     e4m3fn_encode,
     bf16_to_float32,

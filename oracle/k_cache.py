@@ -28,6 +28,7 @@ code table), its own bf16 widening and its own record addressing.
 import numpy as np
 
 from .fp8 import E4M3FN_TABLE
+from .layout import preshuffled_offsets
 
 E4M3FN_MAX = 448.0
 _POS_VALUES = E4M3FN_TABLE[:0x7F]  # codes 0x00..0x7E: every finite value >= 0, increasing
@@ -84,10 +85,13 @@ def record_offset(slot: int, head_dim: int) -> int:
     return int(slot) * (int(head_dim) + 4)
 
 
-def write_k_cache(pool: np.ndarray, k, slot_mapping, head_dim: int) -> np.ndarray:
+def write_k_cache(pool: np.ndarray, k, slot_mapping, head_dim: int, layout: str = "records",
+                  page_size: int = 0) -> np.ndarray:
     """Write the records of rows k [n, head_dim] (float32) at their slots into the
     uint8 pool (in place; returns it).  The pool holds num_slots = len(pool) //
-    (head_dim + 4) rows; slots outside [0, num_slots) are skipped."""
+    (head_dim + 4) rows; slots outside [0, num_slots) are skipped.  With
+    layout="preshuffled" (and the pool's page_size) each token's codes and
+    scale go to the byte offsets ``oracle.layout`` defines instead."""
     k = np.asarray(k, dtype=np.float32)
     codes, scales = quantize_tokens(k)
     rec = head_dim + 4
@@ -95,8 +99,13 @@ def write_k_cache(pool: np.ndarray, k, slot_mapping, head_dim: int) -> np.ndarra
     for i, s in enumerate(np.asarray(slot_mapping, dtype=np.int64).tolist()):
         if s < 0 or s >= num_slots:
             continue
+        sb = np.frombuffer(np.asarray([scales[i]], dtype="<f4").tobytes(), dtype=np.uint8)
+        if layout == "preshuffled":
+            voff, soff = preshuffled_offsets([s], page_size, head_dim)
+            pool[voff[0]] = codes[i]
+            pool[int(soff[0]):int(soff[0]) + 4] = sb
+            continue
         off = record_offset(s, head_dim)
         pool[off:off + head_dim] = codes[i]
-        pool[off + head_dim:off + rec] = np.frombuffer(
-            np.asarray([scales[i]], dtype="<f4").tobytes(), dtype=np.uint8)
+        pool[off + head_dim:off + rec] = sb
     return pool

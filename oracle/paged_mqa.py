@@ -20,6 +20,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 from .fp8 import e4m3fn_to_float64
+from .layout import preshuffled_offsets
 
 NEG_INF_BITS = 0xFF800000
 
@@ -39,14 +40,16 @@ def visible_len(ctx: int, next_n: int, j: int) -> int:
 
 
 def gather_request(kv_cache: np.ndarray, table_row: np.ndarray, ctx: int,
-                   page_size: int, head_dim: int):
+                   page_size: int, head_dim: int, layout: str = "records"):
     """Collect the ``ctx`` tokens of one request through its block table.
 
     Returns (K float64 [ctx, D], scale float64 [ctx]).  Only the first
     ``ceil(ctx/page_size)`` table entries are read; page ids are int64 and the
     byte address ``(id*page_size + slot)*(D+4)`` is formed in 64-bit integers,
     as the int64-id fix requires (ATOM PR #2533 "Address Triton decode KV rows
-    with int64 ids": an int32 id times the row size wraps at 2^31).
+    with int64 ids": an int32 id times the row size wraps at 2^31).  With
+    ``layout="preshuffled"`` the same cache rows are read at the byte offsets
+    ``oracle.layout`` defines.
     """
     ctx = int(ctx)
     rec = head_dim + 4
@@ -56,6 +59,16 @@ def gather_request(kv_cache: np.ndarray, table_row: np.ndarray, ctx: int,
     pages = np.asarray(table_row[:n_pages], dtype=np.int64)
     t = np.arange(ctx, dtype=np.int64)
     rec_index = pages[t // page_size] * np.int64(page_size) + (t % page_size)
+    if layout == "preshuffled":
+        flat = kv_cache.reshape(-1)
+        voff, soff = preshuffled_offsets(rec_index, page_size, head_dim)
+        codes = flat[voff]  # [ctx, D] uint8
+        sb = flat[soff[:, None] + np.arange(4, dtype=np.int64)[None, :]]  # [ctx, 4]
+        k = e4m3fn_to_float64(codes)
+        scale = np.ascontiguousarray(sb).view("<f4").reshape(ctx).astype(np.float64)
+        return k, scale
+    if layout != "records":
+        raise ValueError(f"unknown layout {layout}")
     records = kv_cache.reshape(-1, rec)[rec_index]  # [ctx, D+4] uint8
     k = e4m3fn_to_float64(records[:, :head_dim])
     scale = np.ascontiguousarray(records[:, head_dim:]).view("<f4").reshape(ctx).astype(np.float64)
@@ -105,7 +118,8 @@ def _store(out: np.ndarray, row: int, out_row_stride: int, col0: int,
 def paged_mqa_logits(q, kv_cache, weights, context_lens, block_tables,
                      page_size: int, next_n: int, out: Optional[np.ndarray] = None,
                      out_row_stride: Optional[int] = None,
-                     requests: Optional[Sequence[int]] = None) -> List[Optional[np.ndarray]]:
+                     requests: Optional[Sequence[int]] = None,
+                     layout: str = "records") -> List[Optional[np.ndarray]]:
     """Oracle for the whole logits step.
 
     Returns a list with one fp64 array per output row ``r = b*next_n + j``
@@ -114,7 +128,8 @@ def paged_mqa_logits(q, kv_cache, weights, context_lens, block_tables,
     op writes it: float32 scores on ``[0, visible)``, -inf on
     ``[visible, ctx)``, and no write at ``t >= ctx`` (the reproducer in aiter
     PR #4244 compares only the first ``context_len`` columns; reading adopted:
-    nothing past the context is written).
+    nothing past the context is written).  ``layout`` names the byte layout of
+    ``kv_cache``: "records" (per-token records) or "preshuffled" (``oracle.layout``).
     """
     B = int(np.asarray(context_lens).shape[0])
     q = np.asarray(q)
@@ -123,7 +138,7 @@ def paged_mqa_logits(q, kv_cache, weights, context_lens, block_tables,
     reqs = range(B) if requests is None else requests
     for b in reqs:
         ctx = int(context_lens[b])
-        k, scale = gather_request(kv_cache, block_tables[b], ctx, page_size, D)
+        k, scale = gather_request(kv_cache, block_tables[b], ctx, page_size, D, layout)
         r0 = b * next_n
         res = request_logits(q[r0 : r0 + next_n], weights[r0 : r0 + next_n], k, scale, next_n)
         for j in range(next_n):
