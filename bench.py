@@ -20,7 +20,8 @@ eager steps; `cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample;
 durations from dispatch-recorded events over rotated input sets, their
 throughput and roofline fractions);
 `token_level_tables` times the logits on the same pools read through token-level
-tables (page_size 1); `k_cache_producer` times the K-cache producer
+tables (page_size 1); `preshuffled_layout` (also in each per_config entry)
+times the logits on the same pools rewritten in the preshuffled page layout; `k_cache_producer` times the K-cache producer
 (quantize_k_cache) that writes new K rows into the cache, at a decode step's rows
 and at prefill-sized chunks.
 """
@@ -280,23 +281,25 @@ def warm_set(i, warmup, n_sets):
     return (i - warmup) % n_sets
 
 
-def time_steps(lib, largs, targs, hip, steps, warmup):
+def time_steps(lib, largs, targs, hip, steps, warmup, logits_fn=None):
     """Eager steps (logits then top-k per rotated set): warm-up, then `steps`
-    steps whose kernels record dispatch events.  Returns per-launch ms lists."""
+    steps whose kernels record dispatch events.  Returns per-launch ms lists.
+    `logits_fn` replaces paged_mqa_logits_timed (the preshuffled layout's)."""
     import torch
 
+    lfn = logits_fn or lib.paged_mqa_logits_timed
     n = len(largs)
     spare = [hip.create() for _ in range(4)]
     for i in range(warmup):
         s = warm_set(i, warmup, n)
-        assert lib.paged_mqa_logits_timed(*largs[s], spare[0], spare[1]) == 0
+        assert lfn(*largs[s], spare[0], spare[1]) == 0
         assert lib.topk_per_row_timed(*targs[s], spare[2], spare[3]) == 0
     events = [[hip.create() for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         e = events[i]
-        assert lib.paged_mqa_logits_timed(*largs[i % n], e[0], e[1]) == 0
+        assert lfn(*largs[i % n], e[0], e[1]) == 0
         assert lib.topk_per_row_timed(*targs[i % n], e[2], e[3]) == 0
     torch.cuda.synchronize()
     time_steps.wall_s = time.perf_counter() - t0
@@ -360,9 +363,34 @@ def measure_config(lib, cfg, hip, dev, sh, steps=20, warmup=5):
         "topk_workspace_bytes": ws_bytes,
         "rotated_sets": n_sets, "launches": steps, "generate_s": gen_s,
     }
+    res["preshuffled_layout"] = measure_preshuffled(lib, wl, sets, targs, hip, sh, steps, warmup)
     del sets, ws, largs, targs
     torch.cuda.empty_cache()
     return res
+
+
+def measure_preshuffled(lib, wl, sets, targs, hip, sh, steps=20, warmup=5):
+    """The logits launch on the same pools rewritten in the preshuffled page
+    layout (paged_mqa_logits_preshuffled; bit-identical results), timed as the
+    record layout's."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    pre = torch.from_numpy(synth.preshuffle_pool(wl.kv_cache, wl.page_size)).to(sets[0]["kv"].device)
+    for d in sets:
+        d["kv"].copy_(pre)
+    del pre
+    W = wl.block_tables.shape[1]
+    largs = [(d["q"].data_ptr(), d["kv"].data_ptr(), d["w"].data_ptr(), d["ctx"].data_ptr(),
+              d["tab"].data_ptr(), wl.page_size, wl.next_n, d["out"].data_ptr(),
+              wl.out_row_stride, wl.batch, wl.heads, wl.head_dim, W, sh) for d in sets]
+    torch.cuda.synchronize()
+    lg, _ = time_steps(lib, largs, targs, hip, steps, warmup, lib.paged_mqa_logits_preshuffled_timed)
+    m = float(np.mean(lg)) * 1e-3
+    return {"logits_us": {"mean": m * 1e6, "median": float(np.median(lg)) * 1e3},
+            "logits_roofline": roof_of(wl, m)}
 
 
 def cpu_baseline(wl, min_seconds=10.0, max_reps=400):
@@ -554,6 +582,7 @@ def main():
         res["device_copy"] = measure_copy(dev)
         res["token_level_tables"] = measure_token_level(lib, wl, sets, hip, sh)
         res["k_cache_producer"] = measure_k_cache(lib, wl, hip, dev, sh)
+        res["preshuffled_layout"] = measure_preshuffled(lib, wl, sets, targs, hip, sh, 100, 10)
     if not args.no_per_config:
         del sets, ws, largs, targs
         torch.cuda.empty_cache()

@@ -32,7 +32,9 @@ _LIB_PATH = os.path.join(_PKG, "libpmqa.so")
 _lib: Optional[ctypes.CDLL] = None
 
 # Every symbol include/pmqa.h declares.
-EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "topk_per_row", "topk_per_row_timed",
+EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "paged_mqa_logits_preshuffled",
+           "paged_mqa_logits_preshuffled_timed", "quantize_k_cache_preshuffled",
+           "topk_per_row", "topk_per_row_timed",
            "topk_per_row_workspace_size", "topk_per_row_noalloc", "pmqa_check_inputs",
            "quantize_k_cache",
            "quantize_k_cache_timed", "pmqa_status_string", "pmqa_version", "pmqa_logits_kernel")
@@ -80,6 +82,12 @@ def load_library() -> ctypes.CDLL:
                                      c_i32, c_i64, vp]
     lib.paged_mqa_logits_timed.restype = ctypes.c_int
     lib.paged_mqa_logits_timed.argtypes = lib.paged_mqa_logits.argtypes + [vp, vp]
+    lib.paged_mqa_logits_preshuffled.restype = ctypes.c_int
+    lib.paged_mqa_logits_preshuffled.argtypes = lib.paged_mqa_logits.argtypes
+    lib.paged_mqa_logits_preshuffled_timed.restype = ctypes.c_int
+    lib.paged_mqa_logits_preshuffled_timed.argtypes = lib.paged_mqa_logits_timed.argtypes
+    lib.quantize_k_cache_preshuffled.restype = ctypes.c_int
+    lib.quantize_k_cache_preshuffled.argtypes = [vp, c_i32, vp, c_i32, c_i32, vp, c_i64, c_i32, vp]
     lib.topk_per_row.restype = ctypes.c_int
     lib.topk_per_row.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp, ctypes.c_size_t, vp]
     lib.topk_per_row_timed.restype = ctypes.c_int
@@ -129,7 +137,8 @@ def _byte_view(t: torch.Tensor, name: str) -> torch.Tensor:
 
 def paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
                      context_lens: torch.Tensor, block_tables: torch.Tensor, page_size: int,
-                     next_n: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+                     next_n: int, out: torch.Tensor, stream=None,
+                     layout: str = "records") -> torch.Tensor:
     """Enqueue the logits step; writes ``out`` in place and returns it.
 
     q            [B*next_n, H, 128] or [B, next_n, H, 128], e4m3fn (or its uint8 bytes), contiguous
@@ -138,6 +147,7 @@ def paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Ten
     context_lens [B] int32
     block_tables [B, W] int64, contiguous (W entries per request)
     out          [B*next_n, cols] float32, contiguous (cols = the row stride)
+    layout       "records" (paged_mqa_logits) or "preshuffled" (paged_mqa_logits_preshuffled)
     """
     lib = load_library()
     _byte_view(q, "q")
@@ -169,7 +179,9 @@ def paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Ten
     # a [B, 0] table cannot hold any page: the stride it would pass (1) would
     # let the kernel read an entry the tensor does not have
     _need(ts >= 1 or B == 0, "block_tables must have at least one entry per request")
-    st = lib.paged_mqa_logits(q.data_ptr(), kv_cache.data_ptr(), weights.data_ptr(),
+    _need(layout in ("records", "preshuffled"), f"unknown layout {layout}")
+    fn = lib.paged_mqa_logits if layout == "records" else lib.paged_mqa_logits_preshuffled
+    st = fn(q.data_ptr(), kv_cache.data_ptr(), weights.data_ptr(),
                               context_lens.data_ptr(), block_tables.data_ptr(), int(page_size),
                               int(next_n), out.data_ptr(), int(out.shape[1]), int(B), H, D,
                               int(max(ts, 1)), _stream_handle(out, stream))
@@ -220,7 +232,7 @@ def topk_per_row(logits: torch.Tensor, context_lens: torch.Tensor, k: int, out_i
 
 
 def quantize_k_cache(k: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
-                     stream=None) -> torch.Tensor:
+                     stream=None, page_size: int = 0) -> torch.Tensor:
     """Enqueue the K-cache producer: quantise rows of k into the records of kv_cache
     at their slots (in place; returns kv_cache).
 
@@ -229,6 +241,9 @@ def quantize_k_cache(k: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torc
                  outside the pool (e.g. -1 for padding) are skipped
     kv_cache     page pool bytes (uint8 or float8_e4m3fn, any contiguous shape);
                  its byte size / 132 is the number of cache rows
+    page_size    0: per-token records (quantize_k_cache); otherwise the pool's
+                 page size, writing the preshuffled page layout
+                 (quantize_k_cache_preshuffled)
     """
     lib = load_library()
     _byte_view(kv_cache, "kv_cache")
@@ -240,9 +255,15 @@ def quantize_k_cache(k: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torc
           and slot_mapping.shape[0] == k.shape[0], "slot_mapping must be contiguous int64 [num_tokens]")
     _need(kv_cache.is_contiguous(), "kv_cache must be contiguous")
     num_slots = kv_cache.numel() // (int(k.shape[1]) + 4)
-    st = lib.quantize_k_cache(k.data_ptr(), _K_DTYPES[k.dtype], slot_mapping.data_ptr(),
-                              int(k.shape[0]), int(k.shape[1]), kv_cache.data_ptr(), int(num_slots),
-                              _stream_handle(kv_cache, stream))
+    if page_size:
+        st = lib.quantize_k_cache_preshuffled(k.data_ptr(), _K_DTYPES[k.dtype], slot_mapping.data_ptr(),
+                                              int(k.shape[0]), int(k.shape[1]), kv_cache.data_ptr(),
+                                              int(num_slots), int(page_size),
+                                              _stream_handle(kv_cache, stream))
+    else:
+        st = lib.quantize_k_cache(k.data_ptr(), _K_DTYPES[k.dtype], slot_mapping.data_ptr(),
+                                  int(k.shape[0]), int(k.shape[1]), kv_cache.data_ptr(), int(num_slots),
+                                  _stream_handle(kv_cache, stream))
     _check("quantize_k_cache", st)
     return kv_cache
 

@@ -10,6 +10,11 @@
 // of a token row hold its scale, aiter PR #4244 reproducer).  Slots are int64
 // and the byte offset is formed in 64-bit (ATOM PR #2533: the cache writers
 // address rows by int64 slots).  Slots outside [0, num_slots) are skipped.
+// The same producer can instead write the preshuffled page layout (the same
+// 132 bytes per token, regrouped inside each page into tiles of up to 16
+// tokens: all tokens' first 16 code bytes, then their next 16, ..., then
+// their scales), so that a gather of one token's 16-byte piece across the
+// tile's tokens is one contiguous run.
 //
 // One 16-lane row of a wave per token, 8 elements per lane: the row's amax is
 // a DPP max inside the row (no LDS), the quotient is the IEEE fp32 division,
@@ -95,6 +100,27 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void kcache_kernel(KCacheParam
     int v = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);  // bytes 0, 1
     v = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], v, true);       // bytes 2, 3
     w[h] = (uint32_t)v;
+  }
+  if (p.layout == kLayoutPreshuffled) {
+    // the preshuffled page layout: token u of page g sits in tile u / R
+    // (R = min(page_size, 16) tokens) as its place mm = u % R; the tile holds
+    // piece c (row bytes [16c, 16c+16)) of its R tokens at (c * R + mm) * 16,
+    // then their scales at 128 * R + 4 * mm.  Lane m's 8 codes are half of
+    // piece m / 2.
+    const int lp = p.log2_page;
+    const int64_t page = slot >> lp;
+    const int u = (int)(slot & ((int64_t{1} << lp) - 1));
+    const int lr = lp < 4 ? lp : 4;  // log2 R
+    const int mm = u & ((1 << lr) - 1);
+    uint8_t* tile = p.cache + (page << lp) * (int64_t)kRecordBytes +
+                    (int64_t)((u >> lr) << lr) * kRecordBytes;
+    uint32_t* dst =
+        reinterpret_cast<uint32_t*>(tile + ((((m >> 1) << lr) + mm) * 16) + (m & 1) * 8);
+    dst[0] = w[0];
+    dst[1] = w[1];
+    if (m == 0)
+      *reinterpret_cast<uint32_t*>(tile + (kHeadDim << lr) + 4 * mm) = __float_as_uint(scale);
+    return;
   }
   uint32_t* rec = reinterpret_cast<uint32_t*>(p.cache + slot * (int64_t)kRecordBytes);
   rec[2 * m] = w[0];

@@ -464,8 +464,24 @@ struct ChunkOffsets {
   uint32_t off[kGatherLoads];  // byte offset of the chunk in the iteration's records
 };
 
-__device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
+// Preshuffled pages (kLayoutPreshuffled) instead hold an iteration as one
+// contiguous image of 64 * 132 = 8448 bytes (64 tokens = 4 tiles of 16, each
+// tile's values then its scales), so load i of lane l takes image bytes
+// [1024 i + 16 l, +16); the last load's lanes past the image's 256-byte tail
+// re-read that tail (inside the page) and land in unused slot bytes.
+constexpr int kPreImageBytes = kIterTokens * kRecordBytes;  // 8448
+constexpr int kPreTileBytes = kTile * kRecordBytes;         // 2112
+
+__device__ __forceinline__ ChunkOffsets chunk_offsets(int lane, bool pre = false) {
   ChunkOffsets r;
+  if (pre) {
+#pragma unroll
+    for (int i = 0; i < kGatherLoads; ++i) {
+      const int b = kDmaBytes * i + 16 * lane;
+      r.off[i] = (uint32_t)(b < kPreImageBytes ? b : (kGatherLoads - 1) * kDmaBytes + 16 * (lane & 15));
+    }
+    return r;
+  }
 #pragma unroll
   for (int i = 0; i < kGatherLoads; ++i) {
     const int q = 64 * i + lane;
@@ -492,6 +508,7 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane) {
 //    at or past `limit` fetch a chunk of the pool's first record instead (one
 //    cache line, inside any pool that holds a record) and never use their
 //    page id.
+template <int LAYOUT>
 __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int limit,
                                              const uint32_t* ids_slot, int lane,
                                              const ChunkOffsets& co, uint8_t* slot) {
@@ -520,20 +537,43 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
   int l = lane;
   asm volatile("" : "+v"(l));
   uint32_t rec[kGatherLoads], in_page[kGatherLoads];
+  bool in_image[kGatherLoads];  // the chunk belongs to the iteration's bytes
+  if constexpr (LAYOUT == kLayoutPreshuffled) {
+    // preshuffled pages of 8, 16 or 32 tokens: the image is the iteration's
+    // 64 / page_size pages back to back, each page_size * 132 bytes, i.e.
+    // 33 * page_size / 4 chunks of 16 bytes; chunk c lies in page
+    // j = c / that (a multiply by the host's ceil(2^20 / chunks per page),
+    // exact for every c below 576) at byte 16 (c - j * that) of the page.
+    // rec holds the page's first token (j << log2_page), as read_pages and the
+    // context check below expect; chunks past the image read the pool's
+    // first chunks and land in unused slot bytes.
+    const uint32_t cpp = (33u * (uint32_t)p.page_size) >> 2;
 #pragma unroll
-  for (int i = 0; i < kGatherLoads; ++i) {
-    const int q = 64 * i + l;
-    const int x = q / kChunksPerRecord;
-    const int c = q - x * kChunksPerRecord;
-    rec[i] = (uint32_t)x;
-    in_page[i] = (uint32_t)((x & in_page_mask) * kRecordBytes + (c < 8 ? 16 * c : kRecordBytes - 16));
+    for (int i = 0; i < kGatherLoads; ++i) {
+      const uint32_t c = 64u * i + (uint32_t)l;
+      const uint32_t j = (c * p.pre_magic) >> 20;
+      in_image[i] = c < (uint32_t)(kPreImageBytes / 16);
+      rec[i] = in_image[i] ? j << p.log2_page : 0u;
+      in_page[i] = (c - j * cpp) * 16u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kGatherLoads; ++i) {
+      const int q = 64 * i + l;
+      const int x = q / kChunksPerRecord;
+      const int c = q - x * kChunksPerRecord;
+      rec[i] = (uint32_t)x;
+      in_page[i] = (uint32_t)((x & in_page_mask) * kRecordBytes + (c < 8 ? 16 * c : kRecordBytes - 16));
+      in_image[i] = true;
+    }
   }
   const ChunkPages pg = read_pages(ids_slot, p.log2_page, rec);
   const uint32_t pb = (uint32_t)p.page_bytes;  // <= 32 records
 #pragma unroll
   for (int i = 0; i < kGatherLoads; ++i) {
-    const int64_t off = t0 + (int)rec[i] < limit ? (int64_t)((uint64_t)pg.id[i] * pb + in_page[i])
-                                                 : (int64_t)(16 * (lane & 7));
+    const int64_t off = in_image[i] && t0 + (int)rec[i] < limit
+                            ? (int64_t)((uint64_t)pg.id[i] * pb + in_page[i])
+                            : (int64_t)(16 * (lane & 7));
     __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * kDmaBytes), 16, 0, kStreamK);
   }
 }
@@ -733,6 +773,70 @@ __device__ __forceinline__ SlotOperands read_slot(const uint8_t* slot, int lane)
   return r;
 }
 
+// The iteration's operands from a slot holding a preshuffled image (64
+// tokens as 4 tiles of 2112 bytes: pages of 16 tokens or more hold whole
+// tiles; an 8-token page is half a tile, the tile's two pages 1056 bytes
+// apart).  Lane (m, kq)'s operand is the tile's group (0, kq) and (1, kq)
+// piece of token m: for whole tiles at 16 * lane and 1024 + 16 * lane (the 64
+// lanes read 1 KiB contiguously, no bank conflict), its scale at
+// 2048 + 4 * m; for 8-token pages the same with 8-token groups.  Inline
+// assembly with its own LDS wait, as read_slot.
+__device__ __forceinline__ SlotOperands read_slot_pre(const uint8_t* slot, int lane, int page_size) {
+  static_assert(kPreTileBytes == 2112, "offsets below assume 2112-byte tiles");
+  const int m = lane & 15, kq = lane >> 4;
+  const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)slot);
+  uint32_t av, as, half;
+  if (page_size >= kTile) {
+    av = base + 16u * (uint32_t)lane;
+    half = 1024u;
+    as = base + 2048u + 4u * (uint32_t)m;
+  } else {  // 8-token pages
+    const uint32_t pg = (uint32_t)(m >> 3) * 1056u;
+    av = base + pg + 128u * (uint32_t)kq + 16u * (uint32_t)(m & 7);
+    half = 512u;
+    as = base + pg + 1024u + 4u * (uint32_t)(m & 7);
+  }
+  const uint32_t ah = av + half;
+  u32x4 lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
+  SlotOperands r;
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %12 offset:2112\n\t"
+      "ds_read_b128 %3, %13 offset:2112\n\t"
+      "ds_read_b128 %4, %12 offset:4224\n\t"
+      "ds_read_b128 %5, %13 offset:4224\n\t"
+      "ds_read_b128 %6, %12 offset:6336\n\t"
+      "ds_read_b128 %7, %13 offset:6336\n\t"
+      "ds_read_b32 %8, %14\n\t"
+      "ds_read_b32 %9, %14 offset:2112\n\t"
+      "ds_read_b32 %10, %14 offset:4224\n\t"
+      "ds_read_b32 %11, %14 offset:6336\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo0), "=&v"(hi0), "=&v"(lo1), "=&v"(hi1), "=&v"(lo2), "=&v"(hi2), "=&v"(lo3),
+        "=&v"(hi3), "=&v"(r.sc[0]), "=&v"(r.sc[1]), "=&v"(r.sc[2]), "=&v"(r.sc[3])
+      : "v"(av), "v"(ah), "v"(as)
+      : "memory");
+  const u32x4 lo[kTilesPerIter] = {lo0, lo1, lo2, lo3};
+  const u32x4 hi[kTilesPerIter] = {hi0, hi1, hi2, hi3};
+#pragma unroll
+  for (int tile = 0; tile < kTilesPerIter; ++tile) {
+    r.kb[tile][0] = lo[tile][0]; r.kb[tile][1] = lo[tile][1];
+    r.kb[tile][2] = lo[tile][2]; r.kb[tile][3] = lo[tile][3];
+    r.kb[tile][4] = hi[tile][0]; r.kb[tile][5] = hi[tile][1];
+    r.kb[tile][6] = hi[tile][2]; r.kb[tile][7] = hi[tile][3];
+  }
+  return r;
+}
+
+// The iteration's operands from its slot, in the pool's layout.
+template <int LAYOUT>
+__device__ __forceinline__ SlotOperands read_slot_any(const LogitsParams& p, const uint8_t* slot,
+                                                      int lane) {
+  if constexpr (LAYOUT == kLayoutPreshuffled) return read_slot_pre(slot, lane, p.page_size);
+  else return read_slot(slot, lane);
+}
+
 // Score one iteration from its operands, already read from the slot.
 template <int H, int JW>
 __device__ __forceinline__ void score_ops(const LogitsParams& p, const Run& c, int it, int j0,
@@ -757,10 +861,10 @@ __device__ __forceinline__ void score_ops(const LogitsParams& p, const Run& c, i
   }
 }
 
-template <int H, int JW>
+template <int H, int JW, int LAYOUT>
 __device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int it, int j0, int lane,
                                       const QRegs<H, JW>& qr, const uint8_t* slot) {
-  score_ops<H, JW>(p, c, it, j0, lane, qr, read_slot(slot, lane));
+  score_ops<H, JW>(p, c, it, j0, lane, qr, read_slot_any<LAYOUT>(p, slot, lane));
 }
 
 // H heads; JW next_n rows per wave; WAVES waves per workgroup (one workgroup
@@ -777,7 +881,7 @@ __device__ __forceinline__ void score(const LogitsParams& p, const Run& c, int i
 // refill(k-R) before the gather of k, so "gather k has landed" (the vector
 // memory counter drains in order) also proves they have landed.  Ids of
 // iteration j live in id slot j % 2R, values in ring slot j % R.
-template <int H, int JW, int WAVES, int RING>
+template <int H, int JW, int WAVES, int RING, int LAYOUT>
 __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __restrict__ ctx_lens,
                                                             int32_t batch, int32_t max_tokens,
                                                             LogitsParams p) {
@@ -830,14 +934,15 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
   // registers to spare (4 waves per CU, or 128 q rows at two waves per SIMD),
   // recomputed at each gather otherwise (an opaque copy of the lane index keeps
   // the compiler from hoisting them)
-  const ChunkOffsets co_kept = chunk_offsets(lane);
+  constexpr bool pre = LAYOUT == kLayoutPreshuffled;
+  const ChunkOffsets co_kept = chunk_offsets(lane, pre);
   auto offsets = [&]() -> ChunkOffsets {
     if constexpr (WAVES <= 4 || (WAVES == 8 && H * JW == 128)) {
       return co_kept;
     } else {
       int l = lane;
       asm volatile("" : "+v"(l));
-      return chunk_offsets(l);
+      return chunk_offsets(l, pre);
     }
   };
 
@@ -855,7 +960,7 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
       issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kMaxPages);
       ++n_ids;
     }
-    issue_gather(p, run.it0 + s, s < n_it ? run.ctx_eff : 0, my_ids + s * kMaxPages, lane,
+    issue_gather<LAYOUT>(p, run.it0 + s, s < n_it ? run.ctx_eff : 0, my_ids + s * kMaxPages, lane,
                  offsets(), my_ring + s * kSlotBytes);
   }
   // with one slot, the first score waits for every load anyway: q behind the
@@ -871,7 +976,7 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
       // page-id loads and stores issued in between only add to the count):
       // once at most that many are outstanding, iteration k's data has landed
       wait_vm(kGatherLoads * min(RING - 1, n_span - 1 - k));
-      score<H, JW>(p, run, run.it0 + k, j0, lane, qr, my_ring + s * kSlotBytes);
+      score<H, JW, LAYOUT>(p, run, run.it0 + k, j0, lane, qr, my_ring + s * kSlotBytes);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot reads done before refill
       if (k + RING < n_it) {
         // refill(k): ids of iteration k + 2R, then the gather of k + R
@@ -879,7 +984,7 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
           issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kMaxPages);
           ++n_ids;
         }
-        issue_gather(p, run.it0 + k + RING, run.ctx_eff,
+        issue_gather<LAYOUT>(p, run.it0 + k + RING, run.ctx_eff,
                      my_ids + ((k + RING) % (2 * RING)) * kMaxPages, lane, offsets(),
                      my_ring + s * kSlotBytes);
       }
@@ -896,7 +1001,7 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
 // the gather of k, so the owner's wait for gather k proves them landed before
 // their own gather is issued (L >= RING - 1).  Every wave of a workgroup runs
 // the same run, hence the same number of barriers.
-template <int H, int G, int RING>
+template <int H, int G, int RING, int LAYOUT>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void logits_shared_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t max_tokens,
                           LogitsParams p) {
@@ -929,7 +1034,7 @@ void logits_shared_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, i
     return;
   }
   const int n_it = run.n_it;
-  const ChunkOffsets co = chunk_offsets(lane);
+  const ChunkOffsets co = chunk_offsets(lane, LAYOUT == kLayoutPreshuffled);
   for (int k = wl; k < L; k += G)
     if (k < n_it) issue_ids(p, run, run.it0 + k, lane, id_slot(k));
   QRegs<H, 1> qr;
@@ -938,7 +1043,7 @@ void logits_shared_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, i
   for (int k = wl; k < RING - 1; k += G) {
     if (k >= n_it) break;
     if (k + L < n_it) issue_ids(p, run, run.it0 + k + L, lane, id_slot(k + L));
-    issue_gather(p, run.it0 + k, run.ctx_eff, id_slot(k), lane, co, &ring[k % RING][0]);
+    issue_gather<LAYOUT>(p, run.it0 + k, run.ctx_eff, id_slot(k), lane, co, &ring[k % RING][0]);
   }
   for (int k = 0; k < n_it; ++k) {
     if (k % G == wl) {
@@ -950,9 +1055,9 @@ void logits_shared_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, i
     const int nx = k + RING - 1;
     if (nx < n_it && nx % G == wl) {
       if (nx + L < n_it) issue_ids(p, run, run.it0 + nx + L, lane, id_slot(nx + L));
-      issue_gather(p, run.it0 + nx, run.ctx_eff, id_slot(nx), lane, co, &ring[nx % RING][0]);
+      issue_gather<LAYOUT>(p, run.it0 + nx, run.ctx_eff, id_slot(nx), lane, co, &ring[nx % RING][0]);
     }
-    score<H, 1>(p, run, run.it0 + k, wl, lane, qr, &ring[k % RING][0]);
+    score<H, 1, LAYOUT>(p, run, run.it0 + k, wl, lane, qr, &ring[k % RING][0]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
@@ -1029,7 +1134,7 @@ __device__ __forceinline__ Run next_item(const CtxArgs& a, const Run& cur, uint3
   return item_run(a, b, ctx, it0);
 }
 
-template <int H, int JW>
+template <int H, int JW, int LAYOUT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t max_tokens,
                         const int64_t* __restrict__ tables, int32_t warm_lines,
@@ -1111,7 +1216,7 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
     load_q_lines<H, JW>(p, cur.b, lane, kq, ql, qr);
     asm volatile("" ::: "memory");  // every q load is issued before the gather
     const int64_t id0 = page_id(p, cur);
-    gather_page(p, cur.it0, id0, lane, chunk_offsets(lane), slot);
+    gather_page(p, cur.it0, id0, lane, chunk_offsets(lane, LAYOUT == kLayoutPreshuffled), slot);
     // the q loads have landed once at most the gather's loads are left (the
     // vector memory counter drains in order); the compiler would drain the
     // gather too
@@ -1123,7 +1228,7 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
       id1 = page_id(p, nxt);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the gather
-    score<H, JW>(p, cur, cur.it0, 0, lane, qr, slot);
+    score<H, JW, LAYOUT>(p, cur, cur.it0, 0, lane, qr, slot);
     if (cnt == 1) return;
     // the slot reads are done (read_slot waits for them): refill it.  The next
     // item's fields and the lane pass through empty asm so that its addresses
@@ -1133,18 +1238,18 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
     nxt.it0 = uniform(nxt.it0);
     nxt.b = uniform(nxt.b);
     asm volatile("" : "+v"(l2), "+s"(nxt.it0), "+s"(nxt.b));
-    gather_page(p, nxt.it0, id1, l2, chunk_offsets(l2), slot);
+    gather_page(p, nxt.it0, id1, l2, chunk_offsets(l2, LAYOUT == kLayoutPreshuffled), slot);
     // a second item's q (few waves have one) takes the operand-shaped loads,
     // which need no registers beside the operands
     if (nxt.b != cur.b) load_q<H, JW>(p, nxt.b, 0, m, kq, qr);
     __builtin_amdgcn_s_waitcnt(0);
-    score<H, JW>(p, nxt, nxt.it0, 0, lane, qr, slot);
+    score<H, JW, LAYOUT>(p, nxt, nxt.it0, 0, lane, qr, slot);
     return;
   }
   // smaller pages: the item's page ids are staged in LDS, one per lane
   issue_ids(p, cur, cur.it0, lane, ids[0]);
   __builtin_amdgcn_s_waitcnt(0);  // page ids in LDS
-  issue_gather(p, cur.it0, cur.ctx_eff, ids[0], lane, chunk_offsets(lane), slot);
+  issue_gather<LAYOUT>(p, cur.it0, cur.ctx_eff, ids[0], lane, chunk_offsets(lane, LAYOUT == kLayoutPreshuffled), slot);
   if (cnt > 1) {
     nxt = next_item(ca, cur, e + 1, lane, n0, ctx0, incl0, chunk0);
     issue_ids(p, nxt, nxt.it0, lane, ids[1]);
@@ -1152,7 +1257,7 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   load_q_lines<H, JW>(p, cur.b, lane, kq, ql, qr);
   __builtin_amdgcn_s_waitcnt(0);  // the gather, q and the next item's ids
   {
-    const SlotOperands op = read_slot(slot, lane);
+    const SlotOperands op = read_slot_any<LAYOUT>(p, slot, lane);
     assemble_q<H, JW>(ql, lane, slot, qr);
     score_ops<H, JW>(p, cur, cur.it0, 0, lane, qr, op);
   }
@@ -1162,10 +1267,10 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   nxt.ctx_eff = uniform(nxt.ctx_eff);
   nxt.b = uniform(nxt.b);
   asm volatile("" : "+v"(l2), "+s"(nxt.it0), "+s"(nxt.ctx_eff), "+s"(nxt.b));
-  issue_gather(p, nxt.it0, nxt.ctx_eff, ids[1], l2, chunk_offsets(l2), slot);
+  issue_gather<LAYOUT>(p, nxt.it0, nxt.ctx_eff, ids[1], l2, chunk_offsets(l2, LAYOUT == kLayoutPreshuffled), slot);
   if (nxt.b != cur.b) load_q<H, JW>(p, nxt.b, 0, m, kq, qr);
   __builtin_amdgcn_s_waitcnt(0);
-  score<H, JW>(p, nxt, nxt.it0, 0, lane, qr, slot);
+  score<H, JW, LAYOUT>(p, nxt, nxt.it0, 0, lane, qr, slot);
 }
 
 // Launch geometry per instantiation.  Wave units of at most 64 q rows (and at
@@ -1192,14 +1297,14 @@ struct Geometry {
   static constexpr int kRingDepth = kSmall ? 1 : (kMid ? 2 : 4);
 };
 
-template <int H, int JW>
+template <int H, int JW, int LAYOUT>
 hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t stream) {
   if constexpr (H * JW <= 64) {
     if (p.flat_items > 0) {
       // at most one residency: 16 single-wave workgroups per CU, 32 CUs per XCD
       const int64_t per_xcd = (p.flat_items + 7) / 8;
       const uint32_t n_wg = 8u * (uint32_t)(per_xcd < 16 * 32 ? per_xcd : 16 * 32);
-      auto kern = logits_flat_kernel<H, JW>;
+      auto kern = logits_flat_kernel<H, JW, LAYOUT>;
       const int32_t warm = (int32_t)p.warm_table_lines;  // at most 8192 (a 1 MiB table)
       const int32_t warm_q = (int32_t)p.warm_q_lines;    // at most 32768 (a 4 MiB q)
       if (tm.start || tm.stop)
@@ -1216,7 +1321,7 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
     if (ring > 0) {
       // one unit per workgroup of n_rgroups waves
       const uint32_t n_wg = ((uint32_t)p.n_slices + 7u) & ~7u;
-      auto kern = ring == 8 ? logits_shared_kernel<128, 4, 8> : logits_shared_kernel<128, 2, 4>;
+      auto kern = ring == 8 ? logits_shared_kernel<128, 4, 8, LAYOUT> : logits_shared_kernel<128, 2, 4, LAYOUT>;
       const dim3 block(64 * p.n_rgroups);
       if (tm.start || tm.stop)
         hipExtLaunchKernelGGL(kern, dim3(n_wg), block, 0, stream, tm.start, tm.stop, 0, p.ctx,
@@ -1229,7 +1334,7 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
   using G = Geometry<H, JW>;
   uint32_t n_wg = ((uint32_t)p.n_slices * (uint32_t)p.n_rgroups + G::kWaves - 1) / G::kWaves;
   n_wg = (n_wg + 7u) & ~7u;
-  auto kern = logits_kernel<H, JW, G::kWaves, G::kRingDepth>;
+  auto kern = logits_kernel<H, JW, G::kWaves, G::kRingDepth, LAYOUT>;
   if (tm.start || tm.stop)
     hipExtLaunchKernelGGL(kern, dim3(n_wg), dim3(64 * G::kWaves), 0, stream, tm.start, tm.stop, 0,
                           p.ctx, p.batch, p.max_tokens, p);
@@ -1243,16 +1348,25 @@ hipError_t launch_one(const LogitsParams& p, const LaunchTiming& tm, hipStream_t
 template <int H>
 constexpr int kMaxRows = H >= 128 ? 1 : (H >= 64 ? 3 : 4);
 
+template <int H, int LAYOUT>
+hipError_t launch_rows(const LogitsParams& p, int jw, const LaunchTiming& tm,
+                       hipStream_t stream) {
+  switch (jw) {
+    case 1: return launch_one<H, 1, LAYOUT>(p, tm, stream);
+    case 2: if constexpr (kMaxRows<H> >= 2) return launch_one<H, 2, LAYOUT>(p, tm, stream); break;
+    case 3: if constexpr (kMaxRows<H> >= 3) return launch_one<H, 3, LAYOUT>(p, tm, stream); break;
+    case 4: if constexpr (kMaxRows<H> >= 4) return launch_one<H, 4, LAYOUT>(p, tm, stream); break;
+  }
+  return hipErrorInvalidValue;
+}
+
+// The pool's layout is a template parameter of every kernel, so each layout
+// is compiled on its own (the record layout's kernels keep their registers).
 template <int H>
 hipError_t launch_heads(const LogitsParams& p, int jw, const LaunchTiming& tm,
                         hipStream_t stream) {
-  switch (jw) {
-    case 1: return launch_one<H, 1>(p, tm, stream);
-    case 2: if constexpr (kMaxRows<H> >= 2) return launch_one<H, 2>(p, tm, stream); break;
-    case 3: if constexpr (kMaxRows<H> >= 3) return launch_one<H, 3>(p, tm, stream); break;
-    case 4: if constexpr (kMaxRows<H> >= 4) return launch_one<H, 4>(p, tm, stream); break;
-  }
-  return hipErrorInvalidValue;
+  return p.kv_layout == kLayoutPreshuffled ? launch_rows<H, kLayoutPreshuffled>(p, jw, tm, stream)
+                                           : launch_rows<H, kLayoutRecords>(p, jw, tm, stream);
 }
 
 template <int H>

@@ -127,10 +127,14 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
                         const int32_t* context_lens, const int64_t* block_tables,
                         int32_t page_size, int32_t next_n, float* out, int64_t out_row_stride,
                         int32_t batch, int32_t num_heads, int32_t head_dim,
-                        int64_t block_table_stride, void* stream, const pmqa::LaunchTiming& tm) {
+                        int64_t block_table_stride, void* stream, const pmqa::LaunchTiming& tm,
+                        int kv_layout = pmqa::kLayoutRecords) {
   const pmqa_status sizes = check_logits_sizes(batch, next_n, page_size, out_row_stride, num_heads,
                                                head_dim, block_table_stride);
   if (sizes != PMQA_OK) return sizes;
+  // the preshuffled layout's tiles hold min(page_size, 16) tokens; pages of
+  // 1, 2 or 4 tokens would cut its 16-byte pieces across pages
+  if (kv_layout == pmqa::kLayoutPreshuffled && page_size < 8) return PMQA_ERR_UNSUPPORTED;
   if (batch == 0) return PMQA_OK;
   if (!q || !kv_cache || !weights || !context_lens || !block_tables || !out)
     return PMQA_ERR_NULL;
@@ -152,6 +156,12 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
   p.next_n = next_n;
   p.page_size = page_size;
   p.log2_page = log2_exact(page_size);
+  p.kv_layout = kv_layout;
+  // chunks of a preshuffled 8-32-token page: 33 * page_size / 4; the gather
+  // divides by it as a multiply by ceil(2^20 / it) (exact below 576)
+  p.pre_magic = kv_layout == pmqa::kLayoutPreshuffled && page_size < 64
+                    ? (uint32_t)(((1u << 20) + (33u * page_size / 4u) - 1u) / (33u * page_size / 4u))
+                    : 0u;
   const LogitsPlan pl = plan_logits(batch, next_n, page_size, out_row_stride, num_heads,
                                     block_table_stride);
   p.max_tokens = (int32_t)pl.max_tokens;
@@ -218,8 +228,14 @@ pmqa_status topk_impl(const float* logits, const int32_t* context_lens, int32_t 
 
 pmqa_status kcache_impl(const void* k, int32_t k_dtype, const int64_t* slot_mapping,
                         int32_t num_tokens, int32_t head_dim, void* kv_cache, int64_t num_slots,
-                        void* stream, const pmqa::LaunchTiming& tm) {
+                        void* stream, const pmqa::LaunchTiming& tm,
+                        int layout = pmqa::kLayoutRecords, int32_t page_size = 0) {
   if (num_tokens < 0 || num_slots < 0) return PMQA_ERR_SHAPE;
+  if (layout == pmqa::kLayoutPreshuffled) {
+    if (!valid_page_size(page_size)) return PMQA_ERR_SHAPE;
+    if (page_size < 8) return PMQA_ERR_UNSUPPORTED;
+    if (num_slots % page_size != 0) return PMQA_ERR_SHAPE;  // whole pages only
+  }
   if (k_dtype != PMQA_DTYPE_F32 && k_dtype != PMQA_DTYPE_BF16) return PMQA_ERR_UNSUPPORTED;
   if (head_dim != pmqa::kHeadDim) return PMQA_ERR_UNSUPPORTED;
   if (num_tokens > 0 && (!k || !slot_mapping || (num_slots > 0 && !kv_cache)))
@@ -234,6 +250,8 @@ pmqa_status kcache_impl(const void* k, int32_t k_dtype, const int64_t* slot_mapp
   p.num_slots = num_slots;
   p.num_tokens = num_tokens;
   p.bf16 = k_dtype == PMQA_DTYPE_BF16 ? 1 : 0;
+  p.layout = layout;
+  p.log2_page = layout == pmqa::kLayoutPreshuffled ? log2_exact(page_size) : 0;
   const hipError_t e = pmqa::launch_kcache(p, tm, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
 }
@@ -268,6 +286,37 @@ pmqa_status paged_mqa_logits_timed(const void* q, const void* kv_cache, const fl
   return logits_impl(q, kv_cache, weights, context_lens, block_tables, page_size, next_n, out,
                      out_row_stride, batch, num_heads, head_dim, block_table_stride, stream,
                      timing(start_event, stop_event));
+}
+
+pmqa_status paged_mqa_logits_preshuffled(const void* q, const void* kv_cache,
+                                         const float* weights, const int32_t* context_lens,
+                                         const int64_t* block_tables, int32_t page_size,
+                                         int32_t next_n, float* out, int64_t out_row_stride,
+                                         int32_t batch, int32_t num_heads, int32_t head_dim,
+                                         int64_t block_table_stride, void* stream) {
+  return logits_impl(q, kv_cache, weights, context_lens, block_tables, page_size, next_n, out,
+                     out_row_stride, batch, num_heads, head_dim, block_table_stride, stream,
+                     pmqa::LaunchTiming{}, pmqa::kLayoutPreshuffled);
+}
+
+pmqa_status paged_mqa_logits_preshuffled_timed(const void* q, const void* kv_cache,
+                                               const float* weights, const int32_t* context_lens,
+                                               const int64_t* block_tables, int32_t page_size,
+                                               int32_t next_n, float* out, int64_t out_row_stride,
+                                               int32_t batch, int32_t num_heads, int32_t head_dim,
+                                               int64_t block_table_stride, void* stream,
+                                               void* start_event, void* stop_event) {
+  return logits_impl(q, kv_cache, weights, context_lens, block_tables, page_size, next_n, out,
+                     out_row_stride, batch, num_heads, head_dim, block_table_stride, stream,
+                     timing(start_event, stop_event), pmqa::kLayoutPreshuffled);
+}
+
+pmqa_status quantize_k_cache_preshuffled(const void* k, int32_t k_dtype,
+                                         const int64_t* slot_mapping, int32_t num_tokens,
+                                         int32_t head_dim, void* kv_cache, int64_t num_slots,
+                                         int32_t page_size, void* stream) {
+  return kcache_impl(k, k_dtype, slot_mapping, num_tokens, head_dim, kv_cache, num_slots, stream,
+                     pmqa::LaunchTiming{}, pmqa::kLayoutPreshuffled, page_size);
 }
 
 pmqa_status topk_per_row(const float* logits, const int32_t* context_lens, int32_t k,

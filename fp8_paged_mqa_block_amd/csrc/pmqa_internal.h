@@ -31,7 +31,13 @@ struct LogitsParams {
   int64_t warm_table_lines;  // 128-byte lines of the block table to pull into every XCD's L2
   int64_t warm_q_lines;      // 128-byte lines of q to pull into L2 once (0: none)
   int64_t flat_items;        // > 0: flat geometry over this many possible iterations
+  int32_t kv_layout;         // 0: per-token records; 1: preshuffled pages (8..256 tokens)
+  uint32_t pre_magic;        // preshuffled pages of 8..32 tokens: ceil(2^20 / chunks per page)
 };
+
+// Byte layouts of the page pool (see paged_mqa_logits_preshuffled).
+constexpr int kLayoutRecords = 0;
+constexpr int kLayoutPreshuffled = 1;
 
 // Optional events recorded by the kernel dispatch itself at its start and end.
 struct LaunchTiming {
@@ -111,6 +117,8 @@ struct KCacheParams {
   int64_t num_slots;
   int32_t num_tokens;
   int32_t bf16;            // 1: k holds bf16, 0: fp32
+  int32_t layout;          // kLayoutRecords or kLayoutPreshuffled
+  int32_t log2_page;       // preshuffled: log2(page_size)
 };
 
 hipError_t launch_kcache(const KCacheParams& p, const LaunchTiming& tm, hipStream_t stream);

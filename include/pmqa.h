@@ -117,6 +117,39 @@ PMQA_API pmqa_status paged_mqa_logits(const void* q, const void* kv_cache, const
                              int32_t head_dim, int64_t block_table_stride, void* stream);
 
 /*
+ * paged_mqa_logits_preshuffled - paged_mqa_logits over a pool in the
+ * preshuffled page layout (the pages' kernels read K through a preshuffled
+ * layout built by a library call with (min(page, 16), 16) tiles, aiter PR
+ * #6626 section 1, whose permutation they do not print; this layout is this
+ * library's own, with that tiling).  Same arguments, checks and results as
+ * paged_mqa_logits (bit-identical logits for the same tokens), except:
+ *
+ * kv_cache      the page pool, num_pages pages of page_size * (head_dim + 4)
+ *               bytes, 4-byte aligned.  Page p is cut into tiles of
+ *               R = min(page_size, 16) tokens; tile t starts at byte
+ *               p*page_size*132 + t*R*132.  Inside a tile, for each of the 8
+ *               16-byte pieces c of a token's 128 codes (codes [16c, 16c+16)),
+ *               the pieces of the R tokens follow in token order (piece c of
+ *               the tile's token m at tile byte (c*R + m)*16); then the R
+ *               tokens' fp32 scales, little endian (token m at tile byte
+ *               128*R + 4*m).  quantize_k_cache_preshuffled writes this layout.
+ * page_size     8, 16, 32, 64, 128 or 256 (PMQA_ERR_UNSUPPORTED for 1, 2, 4:
+ *               their pages would split the 16-byte pieces).
+ *
+ * A 64-token step of a request then reads its pages' bytes contiguously and
+ * a matrix-core operand (two 16-byte pieces of one token) from contiguous
+ * LDS bytes across a wave.
+ */
+PMQA_API pmqa_status paged_mqa_logits_preshuffled(const void* q, const void* kv_cache,
+                                                  const float* weights,
+                                                  const int32_t* context_lens,
+                                                  const int64_t* block_tables, int32_t page_size,
+                                                  int32_t next_n, float* out,
+                                                  int64_t out_row_stride, int32_t batch,
+                                                  int32_t num_heads, int32_t head_dim,
+                                                  int64_t block_table_stride, void* stream);
+
+/*
  * topk_per_row - indices of the k largest logits of each row (the follow-on
  * top_k_per_row_decode of aiter PR #4244, first paragraph, which turns each
  * logits row into the sparse-KV index list the caller keeps).
@@ -206,6 +239,12 @@ PMQA_API pmqa_status paged_mqa_logits_timed(const void* q, const void* kv_cache,
                                             int64_t block_table_stride, void* stream,
                                             void* start_event, void* stop_event);
 
+PMQA_API pmqa_status paged_mqa_logits_preshuffled_timed(
+    const void* q, const void* kv_cache, const float* weights, const int32_t* context_lens,
+    const int64_t* block_tables, int32_t page_size, int32_t next_n, float* out,
+    int64_t out_row_stride, int32_t batch, int32_t num_heads, int32_t head_dim,
+    int64_t block_table_stride, void* stream, void* start_event, void* stop_event);
+
 PMQA_API pmqa_status topk_per_row_timed(const float* logits, const int32_t* context_lens,
                                         int32_t k, int32_t* out_idx, int32_t batch,
                                         int32_t next_n, int64_t logits_row_stride,
@@ -280,6 +319,21 @@ PMQA_API pmqa_status quantize_k_cache(const void* k, int32_t k_dtype,
                                       const int64_t* slot_mapping, int32_t num_tokens,
                                       int32_t head_dim, void* kv_cache, int64_t num_slots,
                                       void* stream);
+
+/*
+ * quantize_k_cache_preshuffled - quantize_k_cache writing the preshuffled page
+ * layout that paged_mqa_logits_preshuffled reads: token i's codes and scale
+ * go to the tile positions of cache row slot_mapping[i] (page = slot /
+ * page_size) instead of one 132-byte record.  page_size as for
+ * paged_mqa_logits_preshuffled; num_slots must be a whole number of pages
+ * (PMQA_ERR_SHAPE otherwise).  Other arguments, checks and the quantisation
+ * are those of quantize_k_cache.
+ */
+PMQA_API pmqa_status quantize_k_cache_preshuffled(const void* k, int32_t k_dtype,
+                                                  const int64_t* slot_mapping, int32_t num_tokens,
+                                                  int32_t head_dim, void* kv_cache,
+                                                  int64_t num_slots, int32_t page_size,
+                                                  void* stream);
 
 /* quantize_k_cache with dispatch-recorded start/stop events, as the other _timed calls. */
 PMQA_API pmqa_status quantize_k_cache_timed(const void* k, int32_t k_dtype,

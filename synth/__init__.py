@@ -319,6 +319,23 @@ def make_config(cfg: int, seed: int = 0, table: str = "permuted") -> Workload:
     raise ValueError(f"unknown config {cfg}")
 
 
+def preshuffle_pool(pool: np.ndarray, page_size: int, head_dim: int = 128) -> np.ndarray:
+    """The same pool in the preshuffled page layout (a byte permutation of each
+    page): tiles of R = min(page_size, 16) tokens; a tile holds, for each of the
+    8 16-byte pieces of a 128-byte row (piece g = bytes [16g, 16g+16)), that
+    piece of its R tokens in token order, then the R fp32 scales."""
+    assert head_dim == 128
+    P = int(page_size)
+    R = min(P, 16)
+    rec = head_dim + 4
+    x = np.asarray(pool, dtype=np.uint8).reshape(-1, P // R, R, rec)
+    vals = x[..., :head_dim].reshape(x.shape[0], P // R, R, 8, 16).transpose(0, 1, 3, 2, 4)
+    scl = x[..., head_dim:]
+    tiles = np.concatenate([vals.reshape(x.shape[0], P // R, 8 * R * 16),
+                            scl.reshape(x.shape[0], P // R, R * 4)], axis=2)
+    return np.ascontiguousarray(tiles).reshape(-1)
+
+
 def make_logit_rows(rows: int, width: int, lens: Sequence[int], seed: int = 0,
                     ties: int = 0) -> np.ndarray:
     """Synthetic fp32 score rows for exercising a per-row top-k on its own.

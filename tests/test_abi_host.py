@@ -220,3 +220,15 @@ def test_noalloc_scratch_size_in_header_matches_a_full_split():
     # the long-context workload's full split fits; the MTP workload's stride does not
     assert pm.topk_workspace_size(64, 2048, 131072) <= 32 << 20
     assert pm.topk_workspace_size(1024, 2048, 1 << 20) > 32 << 20
+
+
+@pytest.mark.parametrize("ps,status", [(1, ERR_UNSUPPORTED), (2, ERR_UNSUPPORTED),
+                                       (4, ERR_UNSUPPORTED), (12, ERR_SHAPE), (0, ERR_SHAPE)])
+def test_preshuffled_page_sizes(lib, ps, status):
+    assert lib.paged_mqa_logits_preshuffled(P, P, P, P, P, ps, 1, P, 1024, 2, 64, 128, 16,
+                                            None) == status
+    assert lib.quantize_k_cache_preshuffled(P, 0, P, 4, 128, P, 64, ps, None) == status
+
+
+def test_preshuffled_producer_needs_whole_pages(lib):
+    assert lib.quantize_k_cache_preshuffled(P, 0, P, 4, 128, P, 100, 64, None) == ERR_SHAPE

@@ -253,7 +253,7 @@ def _offset_int32(row_id, row_bytes):
     return v - (1 << 32) if v >= 1 << 31 else v
 
 
-def _gather_int32(kv_cache, table_row, ctx, page_size, head_dim):
+def _gather_int32(kv_cache, table_row, ctx, page_size, head_dim, layout="records"):
     """The oracle's gather with the planted mistake: each record's byte offset is
     the int32 product of its cache row id and the record size.  A wrapped
     (negative) offset lands outside the pool: its values read back as NaN."""
