@@ -87,7 +87,10 @@ constexpr int kMaxPages = kIterTokens;                    // page ids per iterat
 // table, q, weights).  Measured on the decode workload (interleaved with the
 // default policy in one process): 10.56 -> 9.80 us mean per launch; the same
 // on a pool whose pages are contiguous (10.42 -> 9.84 us), which also shows
-// the page scatter itself costs nothing measurable.
+// the page scatter itself costs nothing measurable.  The per-row ring kernel
+// gains more (8-token pages: 149 -> 135 us), but the shared-ring kernel at
+// 128 heads loses 2-3% with it (MTP 314 -> 322 us, long context 113 -> 116 us)
+// and keeps the default policy.
 constexpr int kStreamK = 2;
 
 // A lane's 32 bytes of one 128-byte q row or K record as an MFMA operand:
@@ -508,7 +511,7 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane, bool pre = false
 //    at or past `limit` fetch a chunk of the pool's first record instead (one
 //    cache line, inside any pool that holds a record) and never use their
 //    page id.
-template <int LAYOUT>
+template <int LAYOUT, int CPOL>
 __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int limit,
                                              const uint32_t* ids_slot, int lane,
                                              const ChunkOffsets& co, uint8_t* slot) {
@@ -525,7 +528,7 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
     const uint8_t* src = p.kv + base;
 #pragma unroll
     for (int i = 0; i < kGatherLoads; ++i)
-      __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, kStreamK);
+      __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, CPOL);
     return;
   }
   // Pages here hold at most 32 tokens and the iteration starts at a multiple
@@ -574,13 +577,14 @@ __device__ __forceinline__ void issue_gather(const LogitsParams& p, int it, int 
     const int64_t off = in_image[i] && t0 + (int)rec[i] < limit
                             ? (int64_t)((uint64_t)pg.id[i] * pb + in_page[i])
                             : (int64_t)(16 * (lane & 7));
-    __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * kDmaBytes), 16, 0, kStreamK);
+    __builtin_amdgcn_global_load_lds(p.kv + off, LDS_PTR(slot + i * kDmaBytes), 16, 0, CPOL);
   }
 }
 
 // The gather of one iteration that lies in one page (pages of 64 tokens or
 // more), from that page's id: the same loads as issue_gather's page-sized
 // path.
+template <int CPOL>
 __device__ __forceinline__ void gather_page(const LogitsParams& p, int it, int64_t id, int lane,
                                             const ChunkOffsets& co, uint8_t* slot) {
   const int t0 = it * kIterTokens;
@@ -588,7 +592,7 @@ __device__ __forceinline__ void gather_page(const LogitsParams& p, int it, int64
       p.kv + id * p.page_bytes + (int32_t)((t0 & (p.page_size - 1)) * kRecordBytes);
 #pragma unroll
   for (int i = 0; i < kGatherLoads; ++i)
-    __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, kStreamK);
+    __builtin_amdgcn_global_load_lds(src + co.off[i], LDS_PTR(slot + i * kDmaBytes), 16, 0, CPOL);
 }
 
 // The page id of an iteration that lies in one page, by a scalar load (the
@@ -960,7 +964,7 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
       issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kMaxPages);
       ++n_ids;
     }
-    issue_gather<LAYOUT>(p, run.it0 + s, s < n_it ? run.ctx_eff : 0, my_ids + s * kMaxPages, lane,
+    issue_gather<LAYOUT, kStreamK>(p, run.it0 + s, s < n_it ? run.ctx_eff : 0, my_ids + s * kMaxPages, lane,
                  offsets(), my_ring + s * kSlotBytes);
   }
   // with one slot, the first score waits for every load anyway: q behind the
@@ -984,7 +988,7 @@ __global__ __launch_bounds__(64 * WAVES) void logits_kernel(const int32_t* __res
           issue_ids(p, run, run.it0 + n_ids, lane, my_ids + (n_ids % (2 * RING)) * kMaxPages);
           ++n_ids;
         }
-        issue_gather<LAYOUT>(p, run.it0 + k + RING, run.ctx_eff,
+        issue_gather<LAYOUT, kStreamK>(p, run.it0 + k + RING, run.ctx_eff,
                      my_ids + ((k + RING) % (2 * RING)) * kMaxPages, lane, offsets(),
                      my_ring + s * kSlotBytes);
       }
@@ -1043,7 +1047,7 @@ void logits_shared_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, i
   for (int k = wl; k < RING - 1; k += G) {
     if (k >= n_it) break;
     if (k + L < n_it) issue_ids(p, run, run.it0 + k + L, lane, id_slot(k + L));
-    issue_gather<LAYOUT>(p, run.it0 + k, run.ctx_eff, id_slot(k), lane, co, &ring[k % RING][0]);
+    issue_gather<LAYOUT, 0>(p, run.it0 + k, run.ctx_eff, id_slot(k), lane, co, &ring[k % RING][0]);
   }
   for (int k = 0; k < n_it; ++k) {
     if (k % G == wl) {
@@ -1055,7 +1059,7 @@ void logits_shared_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, i
     const int nx = k + RING - 1;
     if (nx < n_it && nx % G == wl) {
       if (nx + L < n_it) issue_ids(p, run, run.it0 + nx + L, lane, id_slot(nx + L));
-      issue_gather<LAYOUT>(p, run.it0 + nx, run.ctx_eff, id_slot(nx), lane, co, &ring[nx % RING][0]);
+      issue_gather<LAYOUT, 0>(p, run.it0 + nx, run.ctx_eff, id_slot(nx), lane, co, &ring[nx % RING][0]);
     }
     score<H, 1, LAYOUT>(p, run, run.it0 + k, wl, lane, qr, &ring[k % RING][0]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1216,7 +1220,7 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
     load_q_lines<H, JW>(p, cur.b, lane, kq, ql, qr);
     asm volatile("" ::: "memory");  // every q load is issued before the gather
     const int64_t id0 = page_id(p, cur);
-    gather_page(p, cur.it0, id0, lane, chunk_offsets(lane, LAYOUT == kLayoutPreshuffled), slot);
+    gather_page<kStreamK>(p, cur.it0, id0, lane, chunk_offsets(lane, LAYOUT == kLayoutPreshuffled), slot);
     // the q loads have landed once at most the gather's loads are left (the
     // vector memory counter drains in order); the compiler would drain the
     // gather too
@@ -1238,7 +1242,7 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
     nxt.it0 = uniform(nxt.it0);
     nxt.b = uniform(nxt.b);
     asm volatile("" : "+v"(l2), "+s"(nxt.it0), "+s"(nxt.b));
-    gather_page(p, nxt.it0, id1, l2, chunk_offsets(l2, LAYOUT == kLayoutPreshuffled), slot);
+    gather_page<kStreamK>(p, nxt.it0, id1, l2, chunk_offsets(l2, LAYOUT == kLayoutPreshuffled), slot);
     // a second item's q (few waves have one) takes the operand-shaped loads,
     // which need no registers beside the operands
     if (nxt.b != cur.b) load_q<H, JW>(p, nxt.b, 0, m, kq, qr);
@@ -1249,7 +1253,7 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   // smaller pages: the item's page ids are staged in LDS, one per lane
   issue_ids(p, cur, cur.it0, lane, ids[0]);
   __builtin_amdgcn_s_waitcnt(0);  // page ids in LDS
-  issue_gather<LAYOUT>(p, cur.it0, cur.ctx_eff, ids[0], lane, chunk_offsets(lane, LAYOUT == kLayoutPreshuffled), slot);
+  issue_gather<LAYOUT, kStreamK>(p, cur.it0, cur.ctx_eff, ids[0], lane, chunk_offsets(lane, LAYOUT == kLayoutPreshuffled), slot);
   if (cnt > 1) {
     nxt = next_item(ca, cur, e + 1, lane, n0, ctx0, incl0, chunk0);
     issue_ids(p, nxt, nxt.it0, lane, ids[1]);
@@ -1267,7 +1271,7 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
   nxt.ctx_eff = uniform(nxt.ctx_eff);
   nxt.b = uniform(nxt.b);
   asm volatile("" : "+v"(l2), "+s"(nxt.it0), "+s"(nxt.ctx_eff), "+s"(nxt.b));
-  issue_gather<LAYOUT>(p, nxt.it0, nxt.ctx_eff, ids[1], l2, chunk_offsets(l2, LAYOUT == kLayoutPreshuffled), slot);
+  issue_gather<LAYOUT, kStreamK>(p, nxt.it0, nxt.ctx_eff, ids[1], l2, chunk_offsets(l2, LAYOUT == kLayoutPreshuffled), slot);
   if (nxt.b != cur.b) load_q<H, JW>(p, nxt.b, 0, m, kq, qr);
   __builtin_amdgcn_s_waitcnt(0);
   score<H, JW, LAYOUT>(p, nxt, nxt.it0, 0, lane, qr, slot);
