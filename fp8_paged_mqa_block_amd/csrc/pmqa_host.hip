@@ -199,7 +199,7 @@ pmqa_status topk_impl(const float* logits, const int32_t* context_lens, int32_t 
                       void* workspace, size_t workspace_bytes, void* stream,
                       const pmqa::LaunchTiming& tm) {
   if (batch < 0 || next_n < 1 || logits_row_stride < 1) return PMQA_ERR_SHAPE;
-  if (k < 1 || k > 2048) return PMQA_ERR_SHAPE;
+  if (k < 1 || k > pmqa::kTopkMaxK) return PMQA_ERR_SHAPE;
   if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
   if (workspace_bytes > 0 && !workspace) return PMQA_ERR_WORKSPACE;
   if (batch == 0) return PMQA_OK;
@@ -344,7 +344,7 @@ pmqa_status topk_per_row_noalloc(const float* logits, const int32_t* context_len
   // the split topk_per_row makes for rows as long as the stride, in the
   // library's fixed scratch; larger is refused before anything else happens
   if (batch < 0 || next_n < 1 || logits_row_stride < 1) return PMQA_ERR_SHAPE;
-  if (k < 1 || k > 2048) return PMQA_ERR_SHAPE;
+  if (k < 1 || k > pmqa::kTopkMaxK) return PMQA_ERR_SHAPE;
   if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
   const size_t need = topk_per_row_workspace_size(batch * next_n, k, logits_row_stride);
   if (need > pmqa::kTopkScratchBytes) return PMQA_ERR_WORKSPACE;
@@ -357,7 +357,7 @@ pmqa_status topk_per_row_noalloc(const float* logits, const int32_t* context_len
 }
 
 size_t topk_per_row_workspace_size(int32_t rows, int32_t k, int64_t max_row_len) {
-  if (rows < 0 || k < 1 || k > 2048 || max_row_len < 0) return 0;
+  if (rows < 0 || k < 1 || k > pmqa::kTopkMaxK || max_row_len < 0) return 0;
   const int64_t g = pmqa::topk_segment_grid(rows, k, max_row_len, UINT64_MAX);
   return g > 1 ? (size_t)rows * (size_t)g * (size_t)k * 8u : 0u;
 }

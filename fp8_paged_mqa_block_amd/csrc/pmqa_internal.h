@@ -65,6 +65,8 @@ void persistent_geometry(int heads, int rows_per_wave, int* waves, int* ring);
 hipError_t launch_logits(const LogitsParams& p, const LogitsShape& sh, int heads,
                          const LaunchTiming& tm, hipStream_t stream);
 
+// Largest k the top-k accepts (the indexer keeps at most 2048 tokens per row).
+constexpr int kTopkMaxK = 2048;
 // Scores one top-k workgroup selects from registers: a row longer than this is
 // split into segments of at most this many scores (while the workspace has
 // room for their candidates), and a row's merge takes at most this many

@@ -15,6 +15,16 @@
 // equal candidates in list order still takes the lowest indices.  Only the
 // visible scores [0, visible) are read.
 //
+// A list held in registers (up to 16384 scores, 16 a thread) is first tried
+// in one pass on the floats themselves (select_held): value buckets between
+// its smallest and largest score, the threshold bucket, then every score
+// above it staged in LDS at its slot and the threshold bucket's few scores
+// ranked directly.  One CU issues every instruction of a row, so this path
+// keeps a fixed, small number of instructions per score (no per-score
+// branches or ballots).  Lists it cannot resolve that way (a non-finite
+// score, all scores equal, a crowded threshold bucket) and longer rows take
+// the radix passes below.
+//
 // One workgroup's exact select on order-preserving 32-bit keys keeps every
 // step off long LDS round-trip chains, which dominate at these sizes:
 //  * the keys are loaded once into registers (up to 16 a thread); longer
@@ -93,13 +103,21 @@ __device__ __forceinline__ uint32_t high_mask(int low_bits) {
 }
 
 struct TopkShared {
-  uint32_t hist[2][kBins];       // double-buffered histogram
+  // double-buffered histogram; bins kBins + lane take the keys of positions
+  // past the row (rows held as floats), one bin per lane so that their adds
+  // do not serialize on one address; never read
+  uint32_t hist[2][kBins + 64];
   uint32_t part[kWaves];         // per-wave bin totals / row max
   uint32_t part2[kWaves];        // row min
+  uint32_t flags[kWaves];        // per-wave: a non-finite score
   uint32_t col_a[2][kWaves];     // per-wave counts of the final pass, by chunk parity
   uint32_t col_e[2][kWaves];
   alignas(16) uint32_t cand_key[kCandCap];  // keys of the threshold bin, in row order
-  int32_t cand_idx[kCandCap];
+  alignas(16) int32_t cand_idx[kCandCap];
+  // the selection of a row held as floats, in output order; slots kTopkMaxK
+  // + lane take the stores of keys that are not selected
+  int32_t stage_idx[kTopkMaxK + 64];
+  float stage_val[kTopkMaxK + 64];
 };
 
 // Keys of one chunk: thread (wave w, lane l) holds key j of the chunk at
@@ -172,6 +190,10 @@ struct SelectOut {
     idx[slot] = base + i;
     if (val) val[slot] = key_value(key);
   }
+  __device__ __forceinline__ void put_value(uint32_t slot, int32_t i, float v) const {
+    idx[slot] = base + i;
+    if (val) val[slot] = v;
+  }
 };
 
 // A first pass over buckets linear in the score, for rows whose scores are all
@@ -201,6 +223,15 @@ struct Buckets {
   __device__ __forceinline__ uint32_t of(uint32_t key) const {
     const float x = key_value(key);
     return (uint32_t)__builtin_fminf((x - lo) * scale, (float)(kBins - 1));
+  }
+
+  // The bucket of a float as fma(x, scale, -lo * scale), another monotone
+  // non-decreasing function of x (fma rounds once), clamped to [0, kBins - 1]
+  // by one median (x near lo may come out below 0 by the rounding of
+  // -lo * scale).  Rows held as floats bucket every key with this one function.
+  __device__ __forceinline__ uint32_t of_value(float x, float off) const {
+    return (uint32_t)(int)__builtin_amdgcn_fmed3f(__builtin_fmaf(x, scale, off), 0.f,
+                                                  (float)(kBins - 1));
   }
 };
 
@@ -238,6 +269,236 @@ __device__ __forceinline__ void rank_bin_keys(TopkShared& sh, int nc, int remain
   for (int d = 1; d < T; d <<= 1) rank += (uint32_t)__shfl_xor((int)rank, d);
   if (part == 0 && t < nc && rank < (uint32_t)remaining)
     out.put(first_eq + rank, sh.cand_idx[t], sh.cand_key[t]);
+}
+
+// Scores held in registers as floats: thread t holds the KPT consecutive
+// scores at positions t*KPT .. t*KPT + KPT - 1 of the row, segment or
+// candidate list (with IDX, also each score's index in the row), so that a
+// thread-major order of the held scores is their order in the list.  A thread
+// whose scores all lie inside the list loads them as 16-byte vectors; the one
+// thread that straddles its end loads single scores, those past the end
+// reading 0 through the buffer bound (never used).
+template <int KPT, bool IDX>
+struct Held {
+  static_assert(KPT % 4 == 0, "16-byte loads");
+  float x[KPT];
+  int32_t idx[IDX ? KPT : 1];
+
+  __device__ __forceinline__ static void load_words(const void* p, int n, int tb,
+                                                    uint32_t (&w)[KPT]) {
+    const __amdgpu_buffer_rsrc_t rs = Chunk<KPT, IDX>::chunk_rsrc(p, n);
+    if (tb + KPT <= n) {
+#pragma unroll
+      for (int q = 0; q < KPT / 4; ++q) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (tb + 4 * q), 0, 0);
+        w[4 * q] = v[0];
+        w[4 * q + 1] = v[1];
+        w[4 * q + 2] = v[2];
+        w[4 * q + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (tb + j), 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void load(const float* __restrict__ p, int n, int tb) {
+    uint32_t w[KPT];
+    load_words(p, n, tb, w);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) x[j] = __uint_as_float(w[j]);
+  }
+
+  __device__ __forceinline__ void load_idx(const int32_t* __restrict__ ids, int n, int tb) {
+    static_assert(IDX, "scores without indices");
+    uint32_t w[KPT];
+    load_words(ids, n, tb, w);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) idx[j] = (int32_t)w[j];
+  }
+
+  __device__ __forceinline__ int32_t index(int j, int tb) const {
+    if constexpr (IDX) return idx[j];
+    else return tb + j;
+  }
+};
+
+// The top k of n > k scores held as floats, in one bucket pass: value buckets
+// between the smallest and largest score (Buckets), the threshold bucket found
+// from the histogram, then every score above it placed and the threshold
+// bucket's scores ranked against each other.  Every phase is a fixed number of
+// instructions per held score, with no per-score branches or ballots (the
+// costs that dominated: one CU issues the whole row's instructions):
+//  * positions past the list get a negative bucket, which the histogram
+//    counts in an extra bin per lane and every comparison (signed) puts below
+//    all buckets;
+//  * each thread counts its scores above and in the threshold bucket, one
+//    packed prefix sum over the wave and one over the waves give each score's
+//    slot, and the selection is staged in LDS, then stored in order with
+//    coalesced stores;
+//  * the threshold bucket's scores (at most 128) are ranked one per lane, each
+//    compared as one 64-bit value (key above inverted index), so equal scores
+//    take the lowest indices.
+// Returns false, having written nothing, when the row needs radix passes: a
+// non-finite score, all scores equal, or more than 128 scores in a threshold
+// bucket it cannot take whole.  The output is deterministic.
+template <int KPT, bool IDX>
+__device__ __forceinline__ bool select_held(int n, int k, const SelectOut& out, TopkShared& sh,
+                                            const Held<KPT, IDX>& hd) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int tb = tid * KPT;                      // position of the thread's first score
+  const bool full = (wave + 1) * 64 * KPT <= n;  // every position of the wave is inside
+
+  // ---- the largest and smallest score (a non-finite one shows in the sum) ----
+  float mx = -__builtin_inff(), mn = __builtin_inff(), sum = 0.f;
+  auto extremes = [&](auto all) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (decltype(all)::value || tb + j < n) {
+        mx = __builtin_fmaxf(mx, hd.x[j]);
+        mn = __builtin_fminf(mn, hd.x[j]);
+        sum += hd.x[j];
+      }
+    }
+  };
+  if (full) extremes(std::true_type{});
+  else extremes(std::false_type{});
+  const uint32_t wmax = wave_max(order_key(mx));
+  const uint32_t wmin = wave_min(order_key(mn));
+  const bool wbad = __ballot(!__builtin_isfinite(sum)) != 0;
+  if (lane == 0) {
+    sh.part[wave] = wmax;
+    sh.part2[wave] = wmin;
+    sh.flags[wave] = wbad ? 1u : 0u;
+  }
+  reinterpret_cast<uint2*>(sh.hist[0])[tid] = uint2{0u, 0u};
+  __syncthreads();
+  const uint32_t kmax = lane_of(row_max(sh.part[lane & 15]), 0);
+  const uint32_t kmin = lane_of(row_min(sh.part2[lane & 15]), 0);
+  const bool bad = __ballot(lane < 16 && sh.flags[lane] != 0u) != 0;
+  Buckets bk;
+  if (!bad) bk.setup(kmin, kmax);
+  if (!bk.on) {
+    __syncthreads();  // the radix passes reuse what was read above
+    return false;
+  }
+
+  // ---- buckets and their histogram ----
+  const float off = -bk.lo * bk.scale;
+  uint32_t kb[KPT];
+  auto bucket_all = [&](auto all) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      kb[j] = decltype(all)::value || tb + j < n ? bk.of_value(hd.x[j], off) : ~0u;
+  };
+  if (full) bucket_all(std::true_type{});
+  else bucket_all(std::false_type{});
+  uint32_t* h = sh.hist[0];
+  const uint32_t spare = (uint32_t)(kBins + lane);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) atomicAdd(&h[min(kb[j], spare)], 1u);
+  __syncthreads();
+
+  // ---- the bucket holding the k-th score ----
+  const uint2 mine = reinterpret_cast<const uint2*>(h)[tid];  // buckets 2*tid, 2*tid+1
+  const uint32_t wtot = wave_sum(mine.x + mine.y);
+  if (lane == 0) sh.part[wave] = wtot;
+  __syncthreads();
+  const uint32_t pv = sh.part[lane & 15];
+  const uint32_t pw = row_prefix(pv);
+  const uint32_t t16 = lane_of(pw, 15);
+  const uint32_t above_w = t16 - pw;  // scores in higher wave spans
+  const uint64_t fw = __ballot(lane < 16 && above_w < (uint32_t)k && above_w + pv >= (uint32_t)k);
+  const int ws = min((int)__builtin_ctzll(fw), kWaves - 1);
+  const uint32_t base_above = lane_of(above_w, ws);
+  const uint2 hb = reinterpret_cast<const uint2*>(h)[ws * 64 + lane];
+  const uint32_t s2 = hb.x + hb.y;
+  uint32_t t_w;
+  const uint32_t ps = wave_prefix(s2, lane, t_w);
+  const uint32_t above_l = base_above + (t_w - ps);
+  const uint64_t fl = __ballot(above_l < (uint32_t)k && above_l + s2 >= (uint32_t)k);
+  const int ls = min((int)__builtin_ctzll(fl), 63);
+  const uint32_t a = lane_of(above_l, ls);
+  const uint32_t h0 = lane_of(hb.x, ls), h1 = lane_of(hb.y, ls);
+  const uint32_t bin_hi = 2u * (uint32_t)(ws * 64 + ls) + 1u;
+  uint32_t bs, first_eq, cnt;
+  if (a + h1 >= (uint32_t)k) {
+    bs = bin_hi; first_eq = a; cnt = h1;
+  } else {
+    bs = bin_hi - 1u; first_eq = a + h1; cnt = h0;
+  }
+  const uint32_t remaining = (uint32_t)k - first_eq;  // taken from the threshold bucket
+  const bool whole = cnt == remaining;
+  if (!whole && cnt > (uint32_t)kCandCapHeld) {
+    __syncthreads();
+    return false;
+  }
+
+  // ---- each score's slot: above the bucket [0, first_eq), in it after ----
+  uint32_t ca = 0, ce = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    ca += (int)kb[j] > (int)bs ? 1u : 0u;
+    ce += kb[j] == bs ? 1u : 0u;
+  }
+  const uint32_t pk = ca | (ce << 16);  // both counts stay below 2^16
+  uint32_t wpk;
+  const uint32_t incl = wave_prefix(pk, lane, wpk);
+  if (lane == 0) sh.col_a[0][wave] = wpk;
+  const uint32_t nc4 = (cnt + 3u) & ~3u;
+  if (!whole && (uint32_t)tid >= cnt && (uint32_t)tid < nc4) {
+    sh.cand_key[tid] = 0u;  // below every candidate's key
+    sh.cand_idx[tid] = 0;
+  }
+  __syncthreads();
+  const uint32_t wincl = lane_of(row_prefix(sh.col_a[0][lane & 15]), wave);
+  const uint32_t pos = (wincl - wpk) + (incl - pk);
+  uint32_t pa = pos & 0xFFFFu, pe = pos >> 16;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool up = (int)kb[j] > (int)bs;
+    const int32_t ix = hd.index(j, tb);
+    const uint32_t slot = up ? pa : (uint32_t)(kTopkMaxK + lane);
+    sh.stage_idx[slot] = ix;
+    sh.stage_val[slot] = hd.x[j];
+    pa += up ? 1u : 0u;
+    if (kb[j] == bs) {
+      if (whole) {
+        sh.stage_idx[first_eq + pe] = ix;
+        sh.stage_val[first_eq + pe] = hd.x[j];
+      } else {
+        sh.cand_key[pe] = order_key(hd.x[j]);
+        sh.cand_idx[pe] = ix;
+      }
+      ++pe;
+    }
+  }
+  __syncthreads();
+
+  // ---- rank the threshold bucket's scores (score desc, index asc) ----
+  if (!whole && (uint32_t)tid < cnt) {
+    const uint64_t me = ((uint64_t)sh.cand_key[tid] << 32) | (uint32_t)~(uint32_t)sh.cand_idx[tid];
+    uint32_t rank = 0;
+    for (uint32_t i = 0; i < nc4; i += 4) {
+      const uint4 kk = reinterpret_cast<const uint4*>(sh.cand_key)[i >> 2];
+      const uint4 ii = reinterpret_cast<const uint4*>(sh.cand_idx)[i >> 2];
+      rank += ((((uint64_t)kk.x << 32) | (uint32_t)~ii.x) > me) ? 1u : 0u;
+      rank += ((((uint64_t)kk.y << 32) | (uint32_t)~ii.y) > me) ? 1u : 0u;
+      rank += ((((uint64_t)kk.z << 32) | (uint32_t)~ii.z) > me) ? 1u : 0u;
+      rank += ((((uint64_t)kk.w << 32) | (uint32_t)~ii.w) > me) ? 1u : 0u;
+    }
+    if (rank < remaining) {
+      sh.stage_idx[first_eq + rank] = sh.cand_idx[tid];
+      sh.stage_val[first_eq + rank] = key_value(sh.cand_key[tid]);
+    }
+  }
+  __syncthreads();
+
+  // ---- the staged selection, in order ----
+  for (int i = tid; i < k; i += kThreads) out.put_value((uint32_t)i, sh.stage_idx[i], sh.stage_val[i]);
+  return true;
 }
 
 // Selects the row's top k; `ch` holds the row's first chunk (already loaded).
@@ -493,17 +754,43 @@ __device__ __forceinline__ int row_len(const int32_t* __restrict__ ctx_lens, int
   return (int64_t)n > row_stride ? (int)row_stride : n;
 }
 
+// Selects n > k scores held in registers (with IDX, candidates with their
+// row indices at `ids`): one bucket pass when that resolves the row, else the
+// radix passes over the same scores as keys.
+template <int KPT, bool IDX>
+__device__ __forceinline__ void held_or_radix(const float* __restrict__ vals,
+                                              const int32_t* __restrict__ ids, int n, int k,
+                                              const SelectOut& out, TopkShared& sh) {
+  {
+    Held<KPT, IDX> hd;
+    hd.load(vals, n, (int)threadIdx.x * KPT);
+    if constexpr (IDX) hd.load_idx(ids, n, (int)threadIdx.x * KPT);
+    if (select_held<KPT, IDX>(n, k, out, sh, hd)) return;
+  }
+  // the radix passes take the scores again, in their own layout (a rare path:
+  // a non-finite score, all scores equal, or many scores in one bucket)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tb = wave * 64 * KPT + lane;
+  Chunk<KPT, IDX> ch;
+  ch.load(vals, n, 0, tb);
+  if constexpr (IDX) ch.load_idx(ids, n, 0, tb);
+  select_row<KPT, false>(vals, n, k, out, sh, ch);
+}
+
 // Selects n keys at `row` (positions 0..n-1) into `out`, with the register
 // layout their count calls for.  Without STREAM the caller guarantees n <=
-// kTopkSegmentKeys (the keys fit the registers).
-template <bool STREAM>
+// kTopkSegmentKeys (the keys fit the registers).  Without WIDE_HELD, lists of
+// more than 8192 keys skip the one-pass select on floats (its 16 floats and
+// 16 buckets a thread would take the register budget of two workgroups per
+// CU, which the split grid needs) and take the radix passes on keys.
+template <bool STREAM, bool WIDE_HELD = true>
 __device__ __forceinline__ void select_keys(const float* __restrict__ row, int n, int k,
                                             const SelectOut& out, TopkShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (n <= kThreads * kSmallKeys) {
-    Chunk<kSmallKeys> ch;
-    ch.load(row, n, 0, wave * 64 * kSmallKeys + lane);
-    select_row<kSmallKeys, false>(row, n, k, out, sh, ch);
+    held_or_radix<kSmallKeys, false>(row, nullptr, n, k, out, sh);
+  } else if (WIDE_HELD && (!STREAM || n <= kThreads * kLargeKeys)) {
+    held_or_radix<kLargeKeys, false>(row, nullptr, n, k, out, sh);
   } else if (!STREAM || n <= kThreads * kLargeKeys) {
     Chunk<kLargeKeys> ch;
     ch.load(row, n, 0, wave * 64 * kLargeKeys + lane);
@@ -524,7 +811,7 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ row, int n
 // more than one segment per row, a row that would need more segments than
 // the grid has is left to the merge launch, which selects it whole, so the
 // stage keeps only the register-resident layouts.
-template <bool STREAM>
+template <bool STREAM, bool WIDE_HELD = true>
 __device__ __forceinline__ void stage1(const float* __restrict__ logits, int64_t row_stride,
                                        const int32_t* __restrict__ ctx_lens, int32_t next_n,
                                        const TopkParams& p, TopkShared& sh) {
@@ -550,7 +837,7 @@ __device__ __forceinline__ void stage1(const float* __restrict__ logits, int64_t
   const int64_t slot = ((int64_t)r * gridDim.y + s) * k;
   const SelectOut so = nseg == 1 ? SelectOut{out, nullptr, 0}
                                  : SelectOut{p.cand_idx + slot, p.cand_val + slot, (int32_t)s0};
-  select_keys<STREAM>(logits + (int64_t)r * row_stride + s0, (int)(s1 - s0), k, so, sh);
+  select_keys<STREAM, WIDE_HELD>(logits + (int64_t)r * row_stride + s0, (int)(s1 - s0), k, so, sh);
 }
 
 // Stage 1 for grids of one segment per row.  The row pointer, stride, context
@@ -577,7 +864,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
 void topk_split_kernel(const float* __restrict__ logits, int64_t row_stride,
                        const int32_t* __restrict__ ctx_lens, int32_t next_n, TopkParams p) {
   __shared__ TopkShared sh;
-  stage1<false>(logits, row_stride, ctx_lens, next_n, p, sh);
+  stage1<false, false>(logits, row_stride, ctx_lens, next_n, p, sh);
 }
 
 // Stage 2 (launched when the grid has more than one segment per row).
@@ -607,20 +894,8 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __r
   const int64_t slot = (int64_t)r * p.seg_grid * k;
   const float* cv = p.cand_val + slot;
   const int32_t* ci = p.cand_idx + slot;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (m <= kThreads * kSmallKeys) {
-    Chunk<kSmallKeys, true> ch;
-    const int tb = wave * 64 * kSmallKeys + lane;
-    ch.load(cv, m, 0, tb);
-    ch.load_idx(ci, m, 0, tb);
-    select_row<kSmallKeys, false>(cv, m, k, out, sh, ch);
-  } else {
-    Chunk<kLargeKeys, true> ch;
-    const int tb = wave * 64 * kLargeKeys + lane;
-    ch.load(cv, m, 0, tb);
-    ch.load_idx(ci, m, 0, tb);
-    select_row<kLargeKeys, false>(cv, m, k, out, sh, ch);
-  }
+  if (m <= kThreads * kSmallKeys) held_or_radix<kSmallKeys, true>(cv, ci, m, k, out, sh);
+  else held_or_radix<kLargeKeys, true>(cv, ci, m, k, out, sh);
 }
 
 }  // namespace
