@@ -22,8 +22,6 @@ __all__ = [
     "paged_mqa_logits",
     "topk_per_row",
     "topk_workspace_size",
-    "paged_mqa_logits_topk",
-    "logits_topk_workspace_size",
     "check_inputs",
     "quantize_k_cache",
     "EXPORTS",
@@ -38,8 +36,6 @@ EXPORTS = ("paged_mqa_logits", "paged_mqa_logits_timed", "paged_mqa_logits_presh
            "paged_mqa_logits_preshuffled_timed", "quantize_k_cache_preshuffled",
            "topk_per_row", "topk_per_row_timed",
            "topk_per_row_workspace_size", "topk_per_row_noalloc", "pmqa_check_inputs",
-           "paged_mqa_logits_topk", "paged_mqa_logits_topk_timed",
-           "paged_mqa_logits_topk_workspace_size",
            "quantize_k_cache",
            "quantize_k_cache_timed", "pmqa_status_string", "pmqa_version", "pmqa_logits_kernel")
 
@@ -100,13 +96,6 @@ def load_library() -> ctypes.CDLL:
     lib.topk_per_row_noalloc.argtypes = [vp, vp, c_i32, vp, c_i32, c_i32, c_i64, vp]
     lib.topk_per_row_workspace_size.restype = ctypes.c_size_t
     lib.topk_per_row_workspace_size.argtypes = [c_i32, c_i32, c_i64]
-    lib.paged_mqa_logits_topk.restype = ctypes.c_int
-    lib.paged_mqa_logits_topk.argtypes = lib.paged_mqa_logits.argtypes[:-1] + [
-        c_i32, vp, vp, ctypes.c_size_t, vp]
-    lib.paged_mqa_logits_topk_timed.restype = ctypes.c_int
-    lib.paged_mqa_logits_topk_timed.argtypes = lib.paged_mqa_logits_topk.argtypes + [vp, vp]
-    lib.paged_mqa_logits_topk_workspace_size.restype = ctypes.c_size_t
-    lib.paged_mqa_logits_topk_workspace_size.argtypes = [c_i32, c_i32, c_i64]
     lib.pmqa_check_inputs.restype = ctypes.c_int
     lib.pmqa_check_inputs.argtypes = [vp, vp, c_i32, c_i32, c_i64, c_i64, c_i64, vp, vp]
     lib.quantize_k_cache.restype = ctypes.c_int
@@ -146,9 +135,21 @@ def _byte_view(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
-def _logits_args(q, kv_cache, weights, context_lens, block_tables, page_size, next_n, out):
-    """Checks the logits step's tensors; returns the C call's leading arguments
-    (q through block_table_stride)."""
+def paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
+                     context_lens: torch.Tensor, block_tables: torch.Tensor, page_size: int,
+                     next_n: int, out: torch.Tensor, stream=None,
+                     layout: str = "records") -> torch.Tensor:
+    """Enqueue the logits step; writes ``out`` in place and returns it.
+
+    q            [B*next_n, H, 128] or [B, next_n, H, 128], e4m3fn (or its uint8 bytes), contiguous
+    kv_cache     page pool [num_pages, page_size, 132] bytes (any contiguous shape)
+    weights      [B*next_n, H] float32, contiguous
+    context_lens [B] int32
+    block_tables [B, W] int64, contiguous (W entries per request)
+    out          [B*next_n, cols] float32, contiguous (cols = the row stride)
+    layout       "records" (paged_mqa_logits) or "preshuffled" (paged_mqa_logits_preshuffled)
+    """
+    lib = load_library()
     _byte_view(q, "q")
     _byte_view(kv_cache, "kv_cache")
     for name, t in (("q", q), ("kv_cache", kv_cache), ("weights", weights),
@@ -178,69 +179,14 @@ def _logits_args(q, kv_cache, weights, context_lens, block_tables, page_size, ne
     # a [B, 0] table cannot hold any page: the stride it would pass (1) would
     # let the kernel read an entry the tensor does not have
     _need(ts >= 1 or B == 0, "block_tables must have at least one entry per request")
-    return (q.data_ptr(), kv_cache.data_ptr(), weights.data_ptr(), context_lens.data_ptr(),
-            block_tables.data_ptr(), int(page_size), int(next_n), out.data_ptr(), int(out.shape[1]),
-            int(B), H, D, int(max(ts, 1)))
-
-
-def paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
-                     context_lens: torch.Tensor, block_tables: torch.Tensor, page_size: int,
-                     next_n: int, out: torch.Tensor, stream=None,
-                     layout: str = "records") -> torch.Tensor:
-    """Enqueue the logits step; writes ``out`` in place and returns it.
-
-    q            [B*next_n, H, 128] or [B, next_n, H, 128], e4m3fn (or its uint8 bytes), contiguous
-    kv_cache     page pool [num_pages, page_size, 132] bytes (any contiguous shape)
-    weights      [B*next_n, H] float32, contiguous
-    context_lens [B] int32
-    block_tables [B, W] int64, contiguous (W entries per request)
-    out          [B*next_n, cols] float32, contiguous (cols = the row stride)
-    layout       "records" (paged_mqa_logits) or "preshuffled" (paged_mqa_logits_preshuffled)
-    """
-    lib = load_library()
-    args = _logits_args(q, kv_cache, weights, context_lens, block_tables, page_size, next_n, out)
     _need(layout in ("records", "preshuffled"), f"unknown layout {layout}")
     fn = lib.paged_mqa_logits if layout == "records" else lib.paged_mqa_logits_preshuffled
-    _check("paged_mqa_logits", fn(*args, _stream_handle(out, stream)))
+    st = fn(q.data_ptr(), kv_cache.data_ptr(), weights.data_ptr(),
+                              context_lens.data_ptr(), block_tables.data_ptr(), int(page_size),
+                              int(next_n), out.data_ptr(), int(out.shape[1]), int(B), H, D,
+                              int(max(ts, 1)), _stream_handle(out, stream))
+    _check("paged_mqa_logits", st)
     return out
-
-
-def logits_topk_workspace_size(rows: int, k: int, max_row_len: int) -> int:
-    """Workspace bytes of paged_mqa_logits_topk: the row statistics plus the
-    top-k's split of rows up to max_row_len (host only)."""
-    return int(load_library().paged_mqa_logits_topk_workspace_size(int(rows), int(k), int(max_row_len)))
-
-
-def paged_mqa_logits_topk(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
-                          context_lens: torch.Tensor, block_tables: torch.Tensor, page_size: int,
-                          next_n: int, logits: torch.Tensor, k: int, out_idx: torch.Tensor,
-                          workspace: Optional[torch.Tensor] = None,
-                          max_row_len: Optional[int] = None, stream=None) -> torch.Tensor:
-    """Enqueue the fused step (logits with row statistics, then the top-k):
-    writes ``logits`` and ``out_idx`` in place and returns ``out_idx``.
-
-    Tensors as for paged_mqa_logits (``logits`` = out, records layout) and
-    topk_per_row.  ``workspace``: device uint8, at least the row statistics'
-    size; None allocates logits_topk_workspace_size(rows, k, max_row_len)
-    bytes (max_row_len defaulting to the row stride).
-    """
-    lib = load_library()
-    args = _logits_args(q, kv_cache, weights, context_lens, block_tables, page_size, next_n, logits)
-    B = context_lens.shape[0]
-    _need(out_idx.is_cuda and out_idx.dtype == torch.int32 and out_idx.is_contiguous()
-          and tuple(out_idx.shape) == (B * next_n, k), "out_idx must be contiguous int32 [B*next_n, k]")
-    if workspace is None:
-        size = logits_topk_workspace_size(B * next_n, k,
-                                          logits.shape[1] if max_row_len is None else max_row_len)
-        workspace = torch.empty(max(size, 1), dtype=torch.uint8, device=logits.device)
-    _need(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.is_contiguous(),
-          "workspace must be a contiguous uint8 device tensor")
-    nbytes = int(workspace.numel())
-    st = lib.paged_mqa_logits_topk(*args, int(k), out_idx.data_ptr(),
-                                   workspace.data_ptr() if nbytes else None, nbytes,
-                                   _stream_handle(out_idx, stream))
-    _check("paged_mqa_logits_topk", st)
-    return out_idx
 
 
 def topk_workspace_size(rows: int, k: int, max_row_len: int) -> int:

@@ -721,28 +721,6 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
     else if (t < c.ctx_eff)
       orow[t] = neg_inf;
   }
-  // the fused step's row statistics for the top-k: the largest and smallest
-  // visible score of the iteration as order keys (the smallest complemented,
-  // so that both fold in by an unsigned max and a zeroed pair is neutral),
-  // one atomic each per row and wave
-  if (p.row_stats != nullptr) {
-#pragma unroll
-    for (int jj = 0; jj < JW; ++jj) {
-      const int j = j0 + jj;
-      if (j >= p.next_n) break;
-      const int vis = min(max(c.ctx - p.next_n + j + 1, 0), c.ctx_eff);
-      if (vis <= t0) continue;  // no visible token in this iteration (uniform)
-      const uint32_t key = order_key(keep[jj]);
-      const bool in = t < vis;
-      const uint32_t hi = wave_max(in ? key : 0u);
-      const uint32_t lo = wave_max(in ? ~key : 0u);
-      if (lane == 0) {
-        uint32_t* st = p.row_stats + 2 * ((int64_t)c.b * p.next_n + j);
-        atomicMax(st, hi);
-        atomicMax(st + 1, lo);
-      }
-    }
-  }
 }
 
 // The iteration's operands from its LDS slot (record x at x * 144, scale at

@@ -128,7 +128,7 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
                         int32_t page_size, int32_t next_n, float* out, int64_t out_row_stride,
                         int32_t batch, int32_t num_heads, int32_t head_dim,
                         int64_t block_table_stride, void* stream, const pmqa::LaunchTiming& tm,
-                        int kv_layout = pmqa::kLayoutRecords, uint32_t* row_stats = nullptr) {
+                        int kv_layout = pmqa::kLayoutRecords) {
   const pmqa_status sizes = check_logits_sizes(batch, next_n, page_size, out_row_stride, num_heads,
                                                head_dim, block_table_stride);
   if (sizes != PMQA_OK) return sizes;
@@ -157,7 +157,6 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
   p.page_size = page_size;
   p.log2_page = log2_exact(page_size);
   p.kv_layout = kv_layout;
-  p.row_stats = row_stats;
   // chunks of a preshuffled 8-32-token page: 33 * page_size / 4; the gather
   // divides by it as a multiply by ceil(2^20 / it) (exact below 576)
   p.pre_magic = kv_layout == pmqa::kLayoutPreshuffled && page_size < 64
@@ -198,7 +197,7 @@ pmqa_status logits_impl(const void* q, const void* kv_cache, const float* weight
 pmqa_status topk_impl(const float* logits, const int32_t* context_lens, int32_t k,
                       int32_t* out_idx, int32_t batch, int32_t next_n, int64_t logits_row_stride,
                       void* workspace, size_t workspace_bytes, void* stream,
-                      const pmqa::LaunchTiming& tm, uint32_t* row_stats = nullptr) {
+                      const pmqa::LaunchTiming& tm) {
   if (batch < 0 || next_n < 1 || logits_row_stride < 1) return PMQA_ERR_SHAPE;
   if (k < 1 || k > pmqa::kTopkMaxK) return PMQA_ERR_SHAPE;
   if ((int64_t)batch * next_n > INT32_MAX) return PMQA_ERR_SHAPE;
@@ -217,7 +216,6 @@ pmqa_status topk_impl(const float* logits, const int32_t* context_lens, int32_t 
   p.batch = batch;
   p.next_n = next_n;
   p.k = k;
-  p.row_stats = row_stats;
   p.seg_grid = (int32_t)pmqa::topk_segment_grid(rows, k, logits_row_stride, workspace_bytes);
   if (p.seg_grid > 1) {
     const int64_t slots = rows * p.seg_grid * k;
@@ -256,40 +254,6 @@ pmqa_status kcache_impl(const void* k, int32_t k_dtype, const int64_t* slot_mapp
   p.log2_page = layout == pmqa::kLayoutPreshuffled ? log2_exact(page_size) : 0;
   const hipError_t e = pmqa::launch_kcache(p, tm, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PMQA_OK : PMQA_ERR_HIP;
-}
-
-// The fused step: the logits launch folds each row's extremes into the
-// statistics at the start of the workspace, the top-k launch reads them and
-// clears them.  The rest of the workspace bounds the top-k's split as in
-// topk_per_row.
-pmqa_status logits_topk_impl(const void* q, const void* kv_cache, const float* weights,
-                             const int32_t* context_lens, const int64_t* block_tables,
-                             int32_t page_size, int32_t next_n, float* logits,
-                             int64_t logits_row_stride, int32_t batch, int32_t num_heads,
-                             int32_t head_dim, int64_t block_table_stride, int32_t k,
-                             int32_t* out_idx, void* workspace, size_t workspace_bytes,
-                             void* stream, void* start_event, void* stop_event) {
-  const pmqa_status sizes = check_logits_sizes(batch, next_n, page_size, logits_row_stride,
-                                               num_heads, head_dim, block_table_stride);
-  if (sizes != PMQA_OK) return sizes;
-  if (k < 1 || k > pmqa::kTopkMaxK) return PMQA_ERR_SHAPE;
-  const int64_t rows = (int64_t)batch * next_n;
-  const uint64_t stats = pmqa::row_stats_bytes(rows);
-  if (batch > 0 && (!workspace || workspace_bytes < stats)) return PMQA_ERR_WORKSPACE;
-  if (batch == 0) return PMQA_OK;
-  if (!out_idx) return PMQA_ERR_NULL;
-  if (!aligned(workspace, 256) || !aligned(out_idx, 4)) return PMQA_ERR_ALIGNMENT;
-  uint32_t* row_stats = static_cast<uint32_t*>(workspace);
-  uint8_t* rest = static_cast<uint8_t*>(workspace) + stats;
-  pmqa::LaunchTiming t1, t2;
-  t1.start = static_cast<hipEvent_t>(start_event);
-  t2.stop = static_cast<hipEvent_t>(stop_event);
-  pmqa_status st = logits_impl(q, kv_cache, weights, context_lens, block_tables, page_size, next_n,
-                               logits, logits_row_stride, batch, num_heads, head_dim,
-                               block_table_stride, stream, t1, pmqa::kLayoutRecords, row_stats);
-  if (st != PMQA_OK) return st;
-  return topk_impl(logits, context_lens, k, out_idx, batch, next_n, logits_row_stride, rest,
-                   workspace_bytes - stats, stream, t2, row_stats);
 }
 
 pmqa::LaunchTiming timing(void* start_event, void* stop_event) {
@@ -396,38 +360,6 @@ size_t topk_per_row_workspace_size(int32_t rows, int32_t k, int64_t max_row_len)
   if (rows < 0 || k < 1 || k > pmqa::kTopkMaxK || max_row_len < 0) return 0;
   const int64_t g = pmqa::topk_segment_grid(rows, k, max_row_len, UINT64_MAX);
   return g > 1 ? (size_t)rows * (size_t)g * (size_t)k * 8u : 0u;
-}
-
-pmqa_status paged_mqa_logits_topk(const void* q, const void* kv_cache, const float* weights,
-                                  const int32_t* context_lens, const int64_t* block_tables,
-                                  int32_t page_size, int32_t next_n, float* logits,
-                                  int64_t logits_row_stride, int32_t batch, int32_t num_heads,
-                                  int32_t head_dim, int64_t block_table_stride, int32_t k,
-                                  int32_t* out_idx, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
-  return logits_topk_impl(q, kv_cache, weights, context_lens, block_tables, page_size, next_n,
-                          logits, logits_row_stride, batch, num_heads, head_dim,
-                          block_table_stride, k, out_idx, workspace, workspace_bytes, stream,
-                          nullptr, nullptr);
-}
-
-pmqa_status paged_mqa_logits_topk_timed(const void* q, const void* kv_cache, const float* weights,
-                                        const int32_t* context_lens, const int64_t* block_tables,
-                                        int32_t page_size, int32_t next_n, float* logits,
-                                        int64_t logits_row_stride, int32_t batch,
-                                        int32_t num_heads, int32_t head_dim,
-                                        int64_t block_table_stride, int32_t k, int32_t* out_idx,
-                                        void* workspace, size_t workspace_bytes, void* stream,
-                                        void* start_event, void* stop_event) {
-  return logits_topk_impl(q, kv_cache, weights, context_lens, block_tables, page_size, next_n,
-                          logits, logits_row_stride, batch, num_heads, head_dim,
-                          block_table_stride, k, out_idx, workspace, workspace_bytes, stream,
-                          start_event, stop_event);
-}
-
-size_t paged_mqa_logits_topk_workspace_size(int32_t rows, int32_t k, int64_t max_row_len) {
-  if (rows < 0 || k < 1 || k > pmqa::kTopkMaxK || max_row_len < 0) return 0;
-  return (size_t)pmqa::row_stats_bytes(rows) + topk_per_row_workspace_size(rows, k, max_row_len);
 }
 
 pmqa_status quantize_k_cache(const void* k, int32_t k_dtype, const int64_t* slot_mapping,

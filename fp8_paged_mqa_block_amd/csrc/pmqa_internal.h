@@ -33,19 +33,7 @@ struct LogitsParams {
   int64_t flat_items;        // > 0: flat geometry over this many possible iterations
   int32_t kv_layout;         // 0: per-token records; 1: preshuffled pages (8..256 tokens)
   uint32_t pre_magic;        // preshuffled pages of 8..32 tokens: ceil(2^20 / chunks per page)
-  // non-null: per row r, the largest visible score's order key is max-folded
-  // into row_stats[2r] and the complement of the smallest's into row_stats[2r+1]
-  uint32_t* row_stats;
 };
-
-// Order-preserving key of a score: unsigned comparison of keys orders the
-// floats (-0 and +0 share one key; NaN with the sign bit clear sorts above
-// +inf, with it set below -inf).
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u << 1) == 0u) u = 0u;  // -0 and +0 are the same score
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Byte layouts of the page pool (see paged_mqa_logits_preshuffled).
 constexpr int kLayoutRecords = 0;
@@ -97,16 +85,7 @@ struct TopkParams {
   int32_t next_n;
   int32_t k;
   int32_t seg_grid;        // most segments a row is split into (1: no split)
-  // non-null: the row statistics a logits launch folded in (LogitsParams);
-  // the select reads them instead of scanning for its extremes, and leaves
-  // them zero
-  uint32_t* row_stats;
 };
-
-// Bytes of the row statistics at the start of the fused step's workspace:
-// two words per row, rounded up so that the candidates that follow stay
-// 256-byte aligned.
-inline uint64_t row_stats_bytes(int64_t rows) { return ((uint64_t)rows * 8u + 255u) & ~uint64_t{255}; }
 
 // Bytes of the fixed scratch array the allocation-free top-k uses as its
 // workspace (one copy per GPU).

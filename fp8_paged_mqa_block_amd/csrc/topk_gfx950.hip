@@ -78,6 +78,12 @@ constexpr int kCandCapHeld = 128;       // the same, for rows held in registers
 // elements, bounds checked against the record count in bytes.
 constexpr int kBufferFlags = 0x00020000;
 
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) u = 0u;  // -0 and +0 are the same score
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ int lane_rank(uint64_t mask) {
   // number of set bits of mask below this lane
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -265,13 +271,6 @@ __device__ __forceinline__ void rank_bin_keys(TopkShared& sh, int nc, int remain
     out.put(first_eq + rank, sh.cand_idx[t], sh.cand_key[t]);
 }
 
-// A row's extremes as order keys, from the row statistics a logits launch
-// folded in (the fused step); without them the select finds its own.
-struct RowStats {
-  uint32_t kmax = 0u, kmin = 0u;
-  bool have = false;
-};
-
 // Scores held in registers as floats: thread t holds the KPT consecutive
 // scores at positions t*KPT .. t*KPT + KPT - 1 of the row, segment or
 // candidate list (with IDX, also each score's index in the row), so that a
@@ -345,50 +344,40 @@ struct Held {
 // bucket it cannot take whole.  The output is deterministic.
 template <int KPT, bool IDX>
 __device__ __forceinline__ bool select_held(int n, int k, const SelectOut& out, TopkShared& sh,
-                                            const Held<KPT, IDX>& hd, const RowStats& rs) {
+                                            const Held<KPT, IDX>& hd) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int tb = tid * KPT;                      // position of the thread's first score
   const bool full = (wave + 1) * 64 * KPT <= n;  // every position of the wave is inside
 
-  // ---- the largest and smallest score (a non-finite one shows in the sum,
-  // or, from the row statistics, as a key at or beyond an infinity's) ----
-  uint32_t kmax, kmin;
-  bool bad = false;
-  if (rs.have) {
-    kmax = rs.kmax;
-    kmin = rs.kmin;
-    reinterpret_cast<uint2*>(sh.hist[0])[tid] = uint2{0u, 0u};
-    __syncthreads();
-  } else {
-    float mx = -__builtin_inff(), mn = __builtin_inff(), sum = 0.f;
-    auto extremes = [&](auto all) {
+  // ---- the largest and smallest score (a non-finite one shows in the sum) ----
+  float mx = -__builtin_inff(), mn = __builtin_inff(), sum = 0.f;
+  auto extremes = [&](auto all) {
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        if (decltype(all)::value || tb + j < n) {
-          mx = __builtin_fmaxf(mx, hd.x[j]);
-          mn = __builtin_fminf(mn, hd.x[j]);
-          sum += hd.x[j];
-        }
+    for (int j = 0; j < KPT; ++j) {
+      if (decltype(all)::value || tb + j < n) {
+        mx = __builtin_fmaxf(mx, hd.x[j]);
+        mn = __builtin_fminf(mn, hd.x[j]);
+        sum += hd.x[j];
       }
-    };
-    if (full) extremes(std::true_type{});
-    else extremes(std::false_type{});
-    const uint32_t wmax = wave_max(order_key(mx));
-    const uint32_t wmin = wave_min(order_key(mn));
-    const bool wbad = __ballot(!__builtin_isfinite(sum)) != 0;
-    if (lane == 0) {
-      sh.part[wave] = wmax;
-      sh.part2[wave] = wmin;
-      sh.flags[wave] = wbad ? 1u : 0u;
     }
-    reinterpret_cast<uint2*>(sh.hist[0])[tid] = uint2{0u, 0u};
-    __syncthreads();
-    kmax = lane_of(row_max(sh.part[lane & 15]), 0);
-    kmin = lane_of(row_min(sh.part2[lane & 15]), 0);
-    bad = __ballot(lane < 16 && sh.flags[lane] != 0u) != 0;
+  };
+  if (full) extremes(std::true_type{});
+  else extremes(std::false_type{});
+  const uint32_t wmax = wave_max(order_key(mx));
+  const uint32_t wmin = wave_min(order_key(mn));
+  const bool wbad = __ballot(!__builtin_isfinite(sum)) != 0;
+  if (lane == 0) {
+    sh.part[wave] = wmax;
+    sh.part2[wave] = wmin;
+    sh.flags[wave] = wbad ? 1u : 0u;
   }
+  reinterpret_cast<uint2*>(sh.hist[0])[tid] = uint2{0u, 0u};
+  __syncthreads();
+  const uint32_t kmax = lane_of(row_max(sh.part[lane & 15]), 0);
+  const uint32_t kmin = lane_of(row_min(sh.part2[lane & 15]), 0);
+  const bool bad = __ballot(lane < 16 && sh.flags[lane] != 0u) != 0;
   Buckets bk;
   if (!bad) bk.setup(kmin, kmax);
   if (!bk.on) {
@@ -766,7 +755,6 @@ struct TopkArgs {
   float* cand_val;   // workspace: [rows, seg_grid, k] candidate scores
   int32_t* cand_idx;  // workspace: [rows, seg_grid, k] candidate indices
   int32_t seg_grid;   // segments per row in the stage-1 grid (1: no split)
-  uint32_t* row_stats;  // non-null: the fused step's row statistics (TopkParams)
 };
 
 // Visible scores of row r (a row never reads past its stride).
@@ -785,13 +773,12 @@ __device__ __forceinline__ int row_len(const int32_t* __restrict__ ctx_lens, int
 template <int KPT, bool IDX>
 __device__ __forceinline__ void held_or_radix(const float* __restrict__ vals,
                                               const int32_t* __restrict__ ids, int n, int k,
-                                              const SelectOut& out, TopkShared& sh,
-                                              const RowStats& rs = RowStats{}) {
+                                              const SelectOut& out, TopkShared& sh) {
   {
     Held<KPT, IDX> hd;
     hd.load(vals, n, (int)threadIdx.x * KPT);
     if constexpr (IDX) hd.load_idx(ids, n, (int)threadIdx.x * KPT);
-    if (select_held<KPT, IDX>(n, k, out, sh, hd, rs)) return;
+    if (select_held<KPT, IDX>(n, k, out, sh, hd)) return;
   }
   // the radix passes take the scores again, in their own layout (a rare path:
   // a non-finite score, all scores equal, or many scores in one bucket)
@@ -811,13 +798,12 @@ __device__ __forceinline__ void held_or_radix(const float* __restrict__ vals,
 // CU, which the split grid needs) and take the radix passes on keys.
 template <bool STREAM, bool WIDE_HELD = true>
 __device__ __forceinline__ void select_keys(const float* __restrict__ row, int n, int k,
-                                            const SelectOut& out, TopkShared& sh,
-                                            const RowStats& rs = RowStats{}) {
+                                            const SelectOut& out, TopkShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (n <= kThreads * kSmallKeys) {
-    held_or_radix<kSmallKeys, false>(row, nullptr, n, k, out, sh, rs);
+    held_or_radix<kSmallKeys, false>(row, nullptr, n, k, out, sh);
   } else if (WIDE_HELD && (!STREAM || n <= kThreads * kLargeKeys)) {
-    held_or_radix<kLargeKeys, false>(row, nullptr, n, k, out, sh, rs);
+    held_or_radix<kLargeKeys, false>(row, nullptr, n, k, out, sh);
   } else if (!STREAM || n <= kThreads * kLargeKeys) {
     Chunk<kLargeKeys> ch;
     ch.load(row, n, 0, wave * 64 * kLargeKeys + lane);
@@ -845,15 +831,9 @@ __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
   const int n = row_len(a.ctx, r, a.next_n, a.row_stride);
   const int k = a.k;
   int32_t* out = a.out_idx + (int64_t)r * k;
-  // the row statistics are cleared for the next step by workgroup (r, 0)
-  // when rows are not split, else by the merge launch (after every segment
-  // has read them)
-  uint32_t* const st = a.row_stats != nullptr ? a.row_stats + 2 * (int64_t)r : nullptr;
-  const bool clears = st != nullptr && a.seg_grid == 1;
   if (n <= k) {
     if (s == 0)
       for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
-    if (clears && threadIdx.x == 0) *reinterpret_cast<uint2*>(st) = uint2{0u, 0u};
     return;
   }
   const int need = (n + kTopkSegmentKeys - 1) / kTopkSegmentKeys;
@@ -868,16 +848,8 @@ __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
   const int64_t slot = ((int64_t)r * grid + s) * k;
   const SelectOut so = nseg == 1 ? SelectOut{out, nullptr, 0}
                                  : SelectOut{a.cand_idx + slot, a.cand_val + slot, (int32_t)s0};
-  RowStats rs;
-  if (st != nullptr) {
-    const uint2 v = *reinterpret_cast<const uint2*>(st);
-    rs.kmax = v.x;
-    rs.kmin = ~v.y;
-    rs.have = true;
-  }
   select_keys<STREAM, WIDE_HELD>(a.logits + (int64_t)r * a.row_stride + s0, (int)(s1 - s0), k, so,
-                                 sh, rs);
-  if (clears && threadIdx.x == 0) *reinterpret_cast<uint2*>(st) = uint2{0u, 0u};
+                                 sh);
 }
 
 // Stage 1 for grids of one segment per row.  Every parameter is a scalar
@@ -893,10 +865,10 @@ template <bool STREAM>
 __global__ __launch_bounds__(kThreads) void topk_kernel(
     const float* __restrict__ logits, int64_t row_stride, const int32_t* __restrict__ ctx,
     int32_t next_n, int32_t k, int32_t seg_grid, int32_t* __restrict__ out_idx,
-    float* __restrict__ cand_val, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ row_stats) {
+    float* __restrict__ cand_val, int32_t* __restrict__ cand_idx) {
   __shared__ TopkShared sh;
   stage1<STREAM>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val, cand_idx,
-                          seg_grid, row_stats},
+                          seg_grid},
                  sh);
 }
 
@@ -911,11 +883,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80)))
 void topk_split_kernel(const float* __restrict__ logits, int64_t row_stride,
                        const int32_t* __restrict__ ctx, int32_t next_n, int32_t k,
                        int32_t seg_grid, int32_t* __restrict__ out_idx,
-                       float* __restrict__ cand_val, int32_t* __restrict__ cand_idx,
-                       uint32_t* __restrict__ row_stats) {
+                       float* __restrict__ cand_val, int32_t* __restrict__ cand_idx) {
   __shared__ TopkShared sh;
   stage1<false, false>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val, cand_idx,
-                                seg_grid, row_stats},
+                                seg_grid},
                        sh);
 }
 
@@ -928,13 +899,10 @@ void topk_split_kernel(const float* __restrict__ logits, int64_t row_stride,
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     const float* __restrict__ logits, int64_t row_stride, const int32_t* __restrict__ ctx,
     int32_t next_n, int32_t k, int32_t seg_grid, int32_t* __restrict__ out_idx,
-    float* __restrict__ cand_val, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ row_stats) {
+    float* __restrict__ cand_val, int32_t* __restrict__ cand_idx) {
   __shared__ TopkShared sh;
 
   const int r = blockIdx.x;
-  // stage 1 has read the row statistics: clear them for the next step
-  if (row_stats != nullptr && threadIdx.x == 0)
-    *reinterpret_cast<uint2*>(row_stats + 2 * (int64_t)r) = uint2{0u, 0u};
   const int n = row_len(ctx, r, next_n, row_stride);
   if (n <= k) return;
   const int need = (n + kTopkSegmentKeys - 1) / kTopkSegmentKeys;
@@ -998,21 +966,21 @@ hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t 
   if (tm.start || tm.stop)
     hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, tm.start,
                           merge ? nullptr : tm.stop, 0, p.logits, p.row_stride, p.ctx, p.next_n,
-                          p.k, p.seg_grid, p.out_idx, p.cand_val, p.cand_idx, p.row_stats);
+                          p.k, p.seg_grid, p.out_idx, p.cand_val, p.cand_idx);
   else
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, p.logits, p.row_stride, p.ctx,
-                       p.next_n, p.k, p.seg_grid, p.out_idx, p.cand_val, p.cand_idx, p.row_stats);
+                       p.next_n, p.k, p.seg_grid, p.out_idx, p.cand_val, p.cand_idx);
   if (merge) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (tm.start || tm.stop)
       hipExtLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(kThreads), 0, stream, nullptr,
                             tm.stop, 0, p.logits, p.row_stride, p.ctx, p.next_n, p.k, p.seg_grid,
-                            p.out_idx, p.cand_val, p.cand_idx, p.row_stats);
+                            p.out_idx, p.cand_val, p.cand_idx);
     else
       hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(kThreads), 0, stream, p.logits,
                          p.row_stride, p.ctx, p.next_n, p.k, p.seg_grid, p.out_idx, p.cand_val,
-                         p.cand_idx, p.row_stats);
+                         p.cand_idx);
   }
   return hipGetLastError();
 }

@@ -222,52 +222,6 @@ PMQA_API pmqa_status topk_per_row_noalloc(const float* logits, const int32_t* co
 PMQA_API size_t topk_per_row_workspace_size(int32_t rows, int32_t k, int64_t max_row_len);
 
 /*
- * paged_mqa_logits_topk - the indexer step in one call: paged_mqa_logits into
- * `logits`, then topk_per_row of those logits into out_idx (the logits call
- * and its follow-on top_k_per_row_decode that aiter PR #4244's first
- * paragraph describes as one indexer launch).  The logits launch's epilogue
- * also folds each row's largest and smallest visible score into per-row
- * statistics at the start of the workspace, so the top-k launch sets up its
- * value buckets from them instead of first scanning its row for the extremes.
- *
- * Arguments q .. block_table_stride are those of paged_mqa_logits (logits,
- * logits_row_stride = out, out_row_stride), with the records layout; k and
- * out_idx those of topk_per_row.  Results are identical to the two calls.
- * workspace     DEVICE scratch owned by the caller, 256-byte aligned.  Its
- *               first row_stats = 8 * batch * next_n bytes (rounded up to a
- *               multiple of 256) hold the row statistics: the call leaves
- *               them zero, and any other contents on entry cost speed, never
- *               correctness (the buckets stay monotone over any range that
- *               holds the row).  The bytes after them serve the top-k as
- *               topk_per_row's workspace does (they bound the split of rows
- *               longer than 16384 scores, never the result).  Calls that
- *               share a workspace must be ordered on one stream.
- * workspace_bytes  at least the statistics' size, else PMQA_ERR_WORKSPACE
- *               (also for a NULL workspace) and nothing is enqueued;
- *               paged_mqa_logits_topk_workspace_size gives the size with which
- *               rows up to a given length are split fully.
- * Errors are those of the two calls, every one checked before anything is
- * enqueued.
- */
-PMQA_API pmqa_status paged_mqa_logits_topk(const void* q, const void* kv_cache,
-                                           const float* weights, const int32_t* context_lens,
-                                           const int64_t* block_tables, int32_t page_size,
-                                           int32_t next_n, float* logits,
-                                           int64_t logits_row_stride, int32_t batch,
-                                           int32_t num_heads, int32_t head_dim,
-                                           int64_t block_table_stride, int32_t k,
-                                           int32_t* out_idx, void* workspace,
-                                           size_t workspace_bytes, void* stream);
-
-/*
- * paged_mqa_logits_topk_workspace_size - the statistics' bytes for `rows`
- * rows plus topk_per_row_workspace_size(rows, k, max_row_len).  Host only;
- * 0 for invalid arguments.
- */
-PMQA_API size_t paged_mqa_logits_topk_workspace_size(int32_t rows, int32_t k,
-                                                     int64_t max_row_len);
-
-/*
  * paged_mqa_logits_timed, topk_per_row_timed - the same operations, for callers
  * that time each launch (benchmarks, serving telemetry).  start_event and
  * stop_event are caller-created hipEvent_t handles (either may be NULL); they
@@ -296,15 +250,6 @@ PMQA_API pmqa_status topk_per_row_timed(const float* logits, const int32_t* cont
                                         int32_t next_n, int64_t logits_row_stride,
                                         void* workspace, size_t workspace_bytes, void* stream,
                                         void* start_event, void* stop_event);
-
-/* The fused step timed: start_event at the logits dispatch's start, stop_event
- * at the last top-k dispatch's end. */
-PMQA_API pmqa_status paged_mqa_logits_topk_timed(
-    const void* q, const void* kv_cache, const float* weights, const int32_t* context_lens,
-    const int64_t* block_tables, int32_t page_size, int32_t next_n, float* logits,
-    int64_t logits_row_stride, int32_t batch, int32_t num_heads, int32_t head_dim,
-    int64_t block_table_stride, int32_t k, int32_t* out_idx, void* workspace,
-    size_t workspace_bytes, void* stream, void* start_event, void* stop_event);
 
 /*
  * pmqa_check_inputs - debug check of the preconditions that live in device

@@ -115,42 +115,6 @@ def test_topk_workspace_size(lib, rows, k, max_len, want):
     assert pm.topk_workspace_size(rows, k, max_len) == want if rows >= 0 else True
 
 
-def fused(lib, **kw):
-    a = dict(q=P, kv=P, w=P, ctx=P, tab=P, ps=64, nn=1, out=P, ors=1024, b=2, h=64, d=128,
-             ts=16, k=256, idx=P, ws=P, wsb=1 << 16, stream=None)
-    a.update(kw)
-    return lib.paged_mqa_logits_topk(a["q"], a["kv"], a["w"], a["ctx"], a["tab"], a["ps"], a["nn"],
-                                     a["out"], a["ors"], a["b"], a["h"], a["d"], a["ts"], a["k"],
-                                     a["idx"], a["ws"], a["wsb"], a["stream"])
-
-
-@pytest.mark.parametrize("kw,status", [
-    # the logits' checks
-    (dict(q=None), ERR_NULL), (dict(out=None), ERR_NULL), (dict(nn=0), ERR_SHAPE),
-    (dict(ps=24), ERR_SHAPE), (dict(h=48), ERR_UNSUPPORTED), (dict(q=P + 8), ERR_ALIGN),
-    # the top-k's, all before the logits launch
-    (dict(k=0), ERR_SHAPE), (dict(k=2049), ERR_SHAPE), (dict(idx=None), ERR_NULL),
-    (dict(idx=P + 2), ERR_ALIGN),
-    # the row statistics need 8 bytes a row (rounded to 256) in a 256-aligned workspace
-    (dict(ws=None), ERR_WORKSPACE), (dict(wsb=0), ERR_WORKSPACE), (dict(wsb=255), ERR_WORKSPACE),
-    (dict(b=40, wsb=256), ERR_WORKSPACE), (dict(ws=P + 16), ERR_ALIGN),
-    (dict(b=0, ws=None, q=None), OK),
-])
-def test_fused_step_host_checks(lib, kw, status):
-    assert fused(lib, **kw) == status
-
-
-@pytest.mark.parametrize("rows,k,max_len", [(64, 2048, 8192), (64, 2048, 131072), (1024, 2048, 1 << 20),
-                                            (33, 7, 100000), (0, 16, 100)])
-def test_fused_step_workspace_size(lib, rows, k, max_len):
-    stats = (rows * 8 + 255) // 256 * 256
-    want = stats + lib.topk_per_row_workspace_size(rows, k, max_len)
-    assert lib.paged_mqa_logits_topk_workspace_size(rows, k, max_len) == want
-    assert pm.logits_topk_workspace_size(rows, k, max_len) == want
-    assert lib.paged_mqa_logits_topk_workspace_size(-1, k, max_len) == 0
-    assert lib.paged_mqa_logits_topk_workspace_size(rows, 0, max_len) == 0
-
-
 def test_binding_rejects_wrong_dtypes_before_the_library():
     import torch
     t = torch.zeros(4, dtype=torch.float32)
