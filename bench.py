@@ -14,16 +14,18 @@ input set (the kernels back to back, as in a serving forward pass that
 captures every layer's indexer step in one graph); `roofline` describes
 the logits kernel (HBM-bound at this shape), its duration the mean of the
 events its dispatches record at kernel start and end over the same number of
-eager steps; `cpu_baseline` is the CPU oracle (numpy fp64) on a bounded sample;
-`device_copy` is a plain 512 MiB device copy (context for the HBM roofline);
-`per_config` times the other four workloads (logits and top-k launch
-durations from dispatch-recorded events over rotated input sets, their
-throughput and roofline fractions);
-`token_level_tables` times the logits on the same pools read through token-level
-tables (page_size 1); `preshuffled_layout` (also in each per_config entry)
-times the logits on the same pools rewritten in the preshuffled page layout; `k_cache_producer` times the K-cache producer
-(quantize_k_cache) that writes new K rows into the cache, at a decode step's rows
-and at prefill-sized chunks.
+eager steps.  Every timed region follows `settle_s` seconds of untimed steps
+(the GPU's clocks take tens of milliseconds of load to reach their sustained
+level), then the W warm-up steps.  `cpu_baseline` is the CPU oracle (numpy
+fp64) on a bounded sample; `device_copy` is a plain 512 MiB device copy (1 GiB
+moved; context for the HBM roofline); `per_config` times the other four workloads (logits
+and top-k launch durations from dispatch-recorded events over rotated input
+sets, their throughput and roofline fractions); `token_level_tables` times the
+logits on the same pools read through token-level tables (page_size 1);
+`preshuffled_layout` (also in each per_config entry) times the logits on the
+same pools rewritten in the preshuffled page layout; `k_cache_producer` times
+the K-cache producer (quantize_k_cache) that writes new K rows into the cache,
+at a decode step's rows and at prefill-sized chunks.
 """
 import argparse
 import hashlib
@@ -167,8 +169,7 @@ def measure_token_level(lib, wl, sets, hip, sh, reps=100):
     largs = [(d["q"].data_ptr(), d["kv"].data_ptr(), d["w"].data_ptr(), d["ctx"].data_ptr(),
               t.data_ptr(), 1, wl.next_n, d["out"].data_ptr(), wl.out_row_stride, wl.batch,
               wl.heads, wl.head_dim, tok.shape[1], sh) for d, t in zip(sets, tabs)]
-    for i in range(10):
-        assert lib.paged_mqa_logits(*largs[i % len(largs)]) == 0
+    settle(lib, largs, None)
     ev = [(hip.create(), hip.create()) for _ in range(reps)]
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(ev):
@@ -281,6 +282,35 @@ def warm_set(i, warmup, n_sets):
     return (i - warmup) % n_sets
 
 
+# Untimed load before any timed region, in seconds of wall time.  The GPU's
+# clocks reach their sustained level only after tens of milliseconds of
+# load: interleaved rounds of 25 launches measured the MTP workload's logits
+# at 365, 365, 336, 320, 312, 312 us and the long-context workload's at 137,
+# 127, 122, 119, 116, 116 us, so a short timed region right after setup
+# would time the ramp, not the steady state a serving loop runs in.
+SETTLE_S = 0.1
+
+
+def settle(lib, largs, targs, seconds=SETTLE_S, logits_fn=None):
+    """Untimed steps (logits then top-k over the rotated sets; no top-k when
+    targs is None) until `seconds` of wall time have passed; returns the
+    number of steps run.  `logits_fn` replaces paged_mqa_logits."""
+    import torch
+
+    lfn = logits_fn or lib.paged_mqa_logits
+    n = len(largs)
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            assert lfn(*largs[i % n]) == 0
+            if targs is not None:
+                assert lib.topk_per_row(*targs[i % n]) == 0
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def time_steps(lib, largs, targs, hip, steps, warmup, logits_fn=None):
     """Eager steps (logits then top-k per rotated set): warm-up, then `steps`
     steps whose kernels record dispatch events.  Returns per-launch ms lists.
@@ -324,10 +354,11 @@ def roof_of(wl, logits_s):
                 frac=(tflops / FP8_PEAK_TFLOPS) if mfma_bound else (gbps / HBM_PEAK_GBPS))
 
 
-def measure_config(lib, cfg, hip, dev, sh, steps=20, warmup=5):
+def measure_config(lib, cfg, hip, dev, sh, steps=20, warmup=5, rounds=3):
     """One workload's logits and top-k launches, timed eagerly over rotated sets
     (16 for the small decode shape, 3 for the large ones, whose single step
-    already exceeds the last-level cache)."""
+    already exceeds the last-level cache), after the settle phase, over
+    `rounds` rounds of `steps` launches each."""
     import numpy as np
     import torch
 
@@ -340,7 +371,12 @@ def measure_config(lib, cfg, hip, dev, sh, steps=20, warmup=5):
     sets, ws, ws_bytes = make_sets(wl, n_sets, dev)
     largs, targs = launch_args(wl, sets, ws, ws_bytes, sh)
     torch.cuda.synchronize()
-    logits_ms, topk_ms = time_steps(lib, largs, targs, hip, steps, warmup)
+    settle(lib, largs, targs)
+    logits_ms, topk_ms = [], []
+    for _ in range(rounds):
+        lg, tk = time_steps(lib, largs, targs, hip, steps, warmup)
+        logits_ms += lg
+        topk_ms += tk
     lg_s = float(np.mean(logits_ms)) * 1e-3
     tk_s = float(np.mean(topk_ms)) * 1e-3
     roof = roof_of(wl, lg_s)
@@ -361,9 +397,11 @@ def measure_config(lib, cfg, hip, dev, sh, steps=20, warmup=5):
         "topk_hbm_frac": tbytes / tk_s / 1e9 / HBM_PEAK_GBPS,
         "topk_algorithmic_bytes": tbytes,
         "topk_workspace_bytes": ws_bytes,
-        "rotated_sets": n_sets, "launches": steps, "generate_s": gen_s,
+        "rotated_sets": n_sets, "launches": steps * rounds, "settle_s": SETTLE_S,
+        "generate_s": gen_s,
     }
-    res["preshuffled_layout"] = measure_preshuffled(lib, wl, sets, targs, hip, sh, steps, warmup)
+    res["preshuffled_layout"] = measure_preshuffled(lib, wl, sets, targs, hip, sh, steps * rounds,
+                                                    warmup)
     del sets, ws, largs, targs
     torch.cuda.empty_cache()
     return res
@@ -387,6 +425,7 @@ def measure_preshuffled(lib, wl, sets, targs, hip, sh, steps=20, warmup=5):
               d["tab"].data_ptr(), wl.page_size, wl.next_n, d["out"].data_ptr(),
               wl.out_row_stride, wl.batch, wl.heads, wl.head_dim, W, sh) for d in sets]
     torch.cuda.synchronize()
+    settle(lib, largs, targs, logits_fn=lib.paged_mqa_logits_preshuffled)
     lg, _ = time_steps(lib, largs, targs, hip, steps, warmup, lib.paged_mqa_logits_preshuffled_timed)
     m = float(np.mean(lg)) * 1e-3
     return {"logits_us": {"mean": m * 1e6, "median": float(np.median(lg)) * 1e3},
@@ -487,8 +526,9 @@ def main():
     hip = HipEvents()
 
     # Kernel durations: dispatch-recorded start/end events of every launch over
-    # `steps` eager steps (the same rotated inputs).
+    # `steps` eager steps (the same rotated inputs), after the settle phase.
     torch.cuda.synchronize()
+    settle(lib, largs, targs)
     logits_ms, topk_ms = time_steps(lib, largs, targs, hip, args.steps, args.warmup)
     eager_elapsed = time_steps.wall_s
 
@@ -516,6 +556,7 @@ def main():
     warm_graph = capture(lambda i: warm_set(i, nw, len(sets)), nw)
     timed_graph = capture(lambda i: i % len(sets), args.steps)
     torch.cuda.synchronize()
+    settle(lib, largs, targs)  # the captures left the GPU idle
     warm_graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -558,6 +599,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
