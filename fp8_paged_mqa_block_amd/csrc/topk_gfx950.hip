@@ -342,7 +342,7 @@ struct Held {
 // Returns false, having written nothing, when the row needs radix passes: a
 // non-finite score, all scores equal, or more than 128 scores in a threshold
 // bucket it cannot take whole.  The output is deterministic.
-template <int KPT, bool IDX>
+template <int KPT, bool IDX, bool VALS>
 __device__ __forceinline__ bool select_held(int n, int k, const SelectOut& out, TopkShared& sh,
                                             const Held<KPT, IDX>& hd) {
   const int tid = threadIdx.x;
@@ -462,12 +462,12 @@ __device__ __forceinline__ bool select_held(int n, int k, const SelectOut& out, 
     const int32_t ix = hd.index(j, tb);
     const uint32_t slot = up ? pa : (uint32_t)(kTopkMaxK + lane);
     sh.stage_idx[slot] = ix;
-    sh.stage_val[slot] = hd.x[j];
+    if constexpr (VALS) sh.stage_val[slot] = hd.x[j];
     pa += up ? 1u : 0u;
     if (kb[j] == bs) {
       if (whole) {
         sh.stage_idx[first_eq + pe] = ix;
-        sh.stage_val[first_eq + pe] = hd.x[j];
+        if constexpr (VALS) sh.stage_val[first_eq + pe] = hd.x[j];
       } else {
         sh.cand_key[pe] = order_key(hd.x[j]);
         sh.cand_idx[pe] = ix;
@@ -491,13 +491,14 @@ __device__ __forceinline__ bool select_held(int n, int k, const SelectOut& out, 
     }
     if (rank < remaining) {
       sh.stage_idx[first_eq + rank] = sh.cand_idx[tid];
-      sh.stage_val[first_eq + rank] = key_value(sh.cand_key[tid]);
+      if constexpr (VALS) sh.stage_val[first_eq + rank] = key_value(sh.cand_key[tid]);
     }
   }
   __syncthreads();
 
   // ---- the staged selection, in order ----
-  for (int i = tid; i < k; i += kThreads) out.put_value((uint32_t)i, sh.stage_idx[i], sh.stage_val[i]);
+  for (int i = tid; i < k; i += kThreads)
+    out.put_value((uint32_t)i, sh.stage_idx[i], VALS ? sh.stage_val[i] : 0.f);
   return true;
 }
 
@@ -769,8 +770,9 @@ __device__ __forceinline__ int row_len(const int32_t* __restrict__ ctx_lens, int
 
 // Selects n > k scores held in registers (with IDX, candidates with their
 // row indices at `ids`): one bucket pass when that resolves the row, else the
-// radix passes over the same scores as keys.
-template <int KPT, bool IDX>
+// radix passes over the same scores as keys.  VALS: `out` takes the selected
+// scores too (a segment's candidates), else only their indices.
+template <int KPT, bool IDX, bool VALS>
 __device__ __forceinline__ void held_or_radix(const float* __restrict__ vals,
                                               const int32_t* __restrict__ ids, int n, int k,
                                               const SelectOut& out, TopkShared& sh) {
@@ -778,7 +780,7 @@ __device__ __forceinline__ void held_or_radix(const float* __restrict__ vals,
     Held<KPT, IDX> hd;
     hd.load(vals, n, (int)threadIdx.x * KPT);
     if constexpr (IDX) hd.load_idx(ids, n, (int)threadIdx.x * KPT);
-    if (select_held<KPT, IDX>(n, k, out, sh, hd)) return;
+    if (select_held<KPT, IDX, VALS>(n, k, out, sh, hd)) return;
   }
   // the radix passes take the scores again, in their own layout (a rare path:
   // a non-finite score, all scores equal, or many scores in one bucket)
@@ -796,14 +798,14 @@ __device__ __forceinline__ void held_or_radix(const float* __restrict__ vals,
 // more than 8192 keys skip the one-pass select on floats (its 16 floats and
 // 16 buckets a thread would take the register budget of two workgroups per
 // CU, which the split grid needs) and take the radix passes on keys.
-template <bool STREAM, bool WIDE_HELD = true>
+template <bool STREAM, bool WIDE_HELD = true, bool VALS = false>
 __device__ __forceinline__ void select_keys(const float* __restrict__ row, int n, int k,
                                             const SelectOut& out, TopkShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (n <= kThreads * kSmallKeys) {
-    held_or_radix<kSmallKeys, false>(row, nullptr, n, k, out, sh);
+    held_or_radix<kSmallKeys, false, VALS>(row, nullptr, n, k, out, sh);
   } else if (WIDE_HELD && (!STREAM || n <= kThreads * kLargeKeys)) {
-    held_or_radix<kLargeKeys, false>(row, nullptr, n, k, out, sh);
+    held_or_radix<kLargeKeys, false, VALS>(row, nullptr, n, k, out, sh);
   } else if (!STREAM || n <= kThreads * kLargeKeys) {
     Chunk<kLargeKeys> ch;
     ch.load(row, n, 0, wave * 64 * kLargeKeys + lane);
@@ -823,8 +825,10 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ row, int n
 // longer) selects any row whole, streaming it through the registers.  With
 // more than one segment per row, a row that would need more segments than
 // the grid has is left to the merge launch, which selects it whole, so the
-// stage keeps only the register-resident layouts.
-template <bool STREAM, bool WIDE_HELD = true>
+// stage keeps only the register-resident layouts.  SPLIT: the grid may split
+// rows (its segments stage their candidates' scores); otherwise every row
+// is one segment and only indices are staged.
+template <bool STREAM, bool SPLIT>
 __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
   const int r = blockIdx.x;
   const int s = blockIdx.y;
@@ -846,10 +850,16 @@ __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
   // worth, and k <= 2048) select k candidates each into the workspace
   const int64_t s0 = (int64_t)n * s / nseg, s1 = (int64_t)n * (s + 1) / nseg;
   const int64_t slot = ((int64_t)r * grid + s) * k;
-  const SelectOut so = nseg == 1 ? SelectOut{out, nullptr, 0}
-                                 : SelectOut{a.cand_idx + slot, a.cand_val + slot, (int32_t)s0};
-  select_keys<STREAM, WIDE_HELD>(a.logits + (int64_t)r * a.row_stride + s0, (int)(s1 - s0), k, so,
-                                 sh);
+  const float* seg = a.logits + (int64_t)r * a.row_stride + s0;
+  if constexpr (SPLIT) {
+    // one instantiation for both cases (its register budget is that of two
+    // workgroups per CU): a row of one segment stages values it never stores
+    const SelectOut so = nseg == 1 ? SelectOut{out, nullptr, 0}
+                                   : SelectOut{a.cand_idx + slot, a.cand_val + slot, (int32_t)s0};
+    select_keys<false, false, true>(seg, (int)(s1 - s0), k, so, sh);
+  } else {
+    select_keys<STREAM, true, false>(seg, n, k, SelectOut{out, nullptr, 0}, sh);
+  }
 }
 
 // Stage 1 for grids of one segment per row.  Every parameter is a scalar
@@ -857,19 +867,17 @@ __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
 // user SGPRs left beside the argument pointer; the build asks for up to 16),
 // i.e. everything but the candidate indices, which only the last step of a
 // split row writes.  So no wave waits for a scalar load of its argument
-// block, or of the grid size, before its first load.
-// Measured on the decode workload (per-workgroup timestamps): with the
-// parameters in a struct argument, workgroups reached their context-length
-// load 0 - 1.9 us after the first (1.3 us median).
+// block, or of the grid size, before its first load.  Rows here are never
+// split, so no candidate values are staged.
 template <bool STREAM>
 __global__ __launch_bounds__(kThreads) void topk_kernel(
     const float* __restrict__ logits, int64_t row_stride, const int32_t* __restrict__ ctx,
     int32_t next_n, int32_t k, int32_t seg_grid, int32_t* __restrict__ out_idx,
     float* __restrict__ cand_val, int32_t* __restrict__ cand_idx) {
   __shared__ TopkShared sh;
-  stage1<STREAM>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val, cand_idx,
-                          seg_grid},
-                 sh);
+  stage1<STREAM, false>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val, cand_idx,
+                                 seg_grid},
+                        sh);
 }
 
 // Stage 1 for grids that split rows: many workgroups, so two should share a
@@ -885,9 +893,9 @@ void topk_split_kernel(const float* __restrict__ logits, int64_t row_stride,
                        int32_t seg_grid, int32_t* __restrict__ out_idx,
                        float* __restrict__ cand_val, int32_t* __restrict__ cand_idx) {
   __shared__ TopkShared sh;
-  stage1<false, false>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val, cand_idx,
-                                seg_grid},
-                       sh);
+  stage1<false, true>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val, cand_idx,
+                               seg_grid},
+                      sh);
 }
 
 // Stage 2 (launched when the grid has more than one segment per row).
@@ -917,8 +925,8 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
   const int64_t slot = (int64_t)r * seg_grid * k;
   const float* cv = cand_val + slot;
   const int32_t* ci = cand_idx + slot;
-  if (m <= kThreads * kSmallKeys) held_or_radix<kSmallKeys, true>(cv, ci, m, k, out, sh);
-  else held_or_radix<kLargeKeys, true>(cv, ci, m, k, out, sh);
+  if (m <= kThreads * kSmallKeys) held_or_radix<kSmallKeys, true, false>(cv, ci, m, k, out, sh);
+  else held_or_radix<kLargeKeys, true, false>(cv, ci, m, k, out, sh);
 }
 
 }  // namespace
