@@ -261,11 +261,15 @@ def test_topk_synthetic_rows(gpu_lib, ties):
             assert np.all(got[r, m:] == -1)
 
 
-def test_topk_special_rows(gpu_lib):
+@pytest.mark.parametrize("split", [True, False])
+def test_topk_special_rows(gpu_lib, split):
     """Rows the score distribution never produces but the op accepts: one value
     repeated (every key ties), both zeros (equal scores), infinities, subnormals
     and both signs, extremes whose difference overflows, a heavy tail, values a
-    few ulps apart, at lengths on each side of the register-resident limits."""
+    few ulps apart, at lengths on each side of the register-resident limits.
+    With a full workspace the 40000-score rows are split (and the shorter rows
+    go through the split grid); with none, every row is one workgroup's, the
+    shorter rows through the one-pass select on floats and its fallbacks."""
     rng = np.random.default_rng(11)
     rows = []
     for n in (3000, 9000, 40000):
@@ -300,8 +304,9 @@ def test_topk_special_rows(gpu_lib):
     logits = torch.from_numpy(dense).cuda()
     for k in (1, 100, 2048):
         idx = torch.full((len(rows), k), -7, dtype=torch.int32, device="cuda")
-        say(f"[gpu] topk_per_row special rows k={k}")
-        gpu_lib.topk_per_row(logits, ctx, k, idx, next_n=1)
+        say(f"[gpu] topk_per_row special rows k={k} split={split}")
+        ws = None if split else torch.empty(0, dtype=torch.uint8, device="cuda")
+        gpu_lib.topk_per_row(logits, ctx, k, idx, next_n=1, workspace=ws)
         torch.cuda.synchronize()
         want = oracle.topk_per_row(rows, k)
         got = idx.cpu().numpy()
