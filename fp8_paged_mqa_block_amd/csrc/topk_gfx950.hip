@@ -22,8 +22,10 @@
 // ranked directly.  One CU issues every instruction of a row, so this path
 // keeps a fixed, small number of instructions per score (no per-score
 // branches or ballots).  Lists it cannot resolve that way (a non-finite
-// score, all scores equal, a crowded threshold bucket) and longer rows take
-// the radix passes below.
+// score, all scores equal, a crowded threshold bucket), longer rows, and in
+// the split grid lists of more than 8192 scores (whose floats and buckets
+// would exceed the register budget of two workgroups per CU) take the radix
+// passes below.
 //
 // One workgroup's exact select on order-preserving 32-bit keys keeps every
 // step off long LDS round-trip chains, which dominate at these sizes:
