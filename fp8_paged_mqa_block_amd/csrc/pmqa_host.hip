@@ -68,7 +68,11 @@ namespace pmqa {
 int64_t topk_segment_grid(int64_t rows, int32_t k, int64_t max_row_len, uint64_t workspace_bytes) {
   if (rows < 1 || k < 1) return 1;
   if (max_row_len > INT32_MAX) max_row_len = INT32_MAX;
-  int64_t g = (max_row_len + kTopkSegmentKeys - 1) / kTopkSegmentKeys;  // segments a row needs
+  // rows one workgroup holds in registers are never split; longer ones are
+  // cut into segments of at most kTopkSplitKeys scores while the merge has
+  // room for their candidates
+  if (max_row_len <= kTopkSegmentKeys) return 1;
+  int64_t g = (max_row_len + kTopkSplitKeys - 1) / kTopkSplitKeys;  // segments a row needs
   const int64_t merge_cap = kTopkMergeKeys / k;  // the merge holds segments * k candidates
   if (g > merge_cap) g = merge_cap;
   const uint64_t per_segment = (uint64_t)rows * (uint64_t)k * 8u;  // candidates of every row

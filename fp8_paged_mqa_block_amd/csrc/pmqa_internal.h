@@ -73,6 +73,25 @@ constexpr int kTopkMaxK = 2048;
 // candidates (segments * k).
 constexpr int kTopkSegmentKeys = 16384;
 constexpr int kTopkMergeKeys = 16384;
+// Scores a segment of a split row holds when the grid has room: 8 a thread,
+// the layout the one-pass select keeps within the register budget of two
+// workgroups per CU.
+constexpr int kTopkSplitKeys = 8192;
+
+// Segments of a row of n visible scores (n > k) in a stage-1 grid of `grid`
+// segments per row.  1: the grid does not split rows (grid 1), or the row
+// fits one split segment.  Otherwise as many segments of at most
+// kTopkSplitKeys scores as the grid holds; when that is not enough, `grid`
+// segments of at most kTopkSegmentKeys; 0 for a longer row (the merge launch
+// selects it whole).  Every segment of a split row holds more than 4096
+// scores, so more than k <= 2048.
+__host__ __device__ inline int topk_row_segments(int n, int grid) {
+  if (grid <= 1) return 1;
+  const int n_small = (n + kTopkSplitKeys - 1) / kTopkSplitKeys;
+  if (n_small <= grid) return n_small;
+  const int n_large = (n + kTopkSegmentKeys - 1) / kTopkSegmentKeys;
+  return n_large <= grid ? grid : 0;
+}
 
 struct TopkParams {
   const float* logits;
@@ -89,7 +108,7 @@ struct TopkParams {
 
 // Bytes of the fixed scratch array the allocation-free top-k uses as its
 // workspace (one copy per GPU).
-constexpr uint64_t kTopkScratchBytes = uint64_t{32} << 20;
+constexpr uint64_t kTopkScratchBytes = uint64_t{64} << 20;
 // This device's copy of that array (looked up once per device).
 hipError_t topk_scratch(void** ptr);
 

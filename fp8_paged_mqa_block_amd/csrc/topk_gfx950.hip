@@ -5,11 +5,12 @@
 // among its visible tokens [0, visible(r)), -1 in the slots left over.
 //
 // Work split.  A row of up to 16384 scores is selected by one 1024-thread
-// workgroup.  A longer row is cut into nseg nearly equal segments (at most
-// the grid's second dimension, which the caller's workspace bounds), each
-// selected by its own workgroup into k candidates (score, index) in the
-// workspace; a second launch then selects the row's top k among its nseg * k
-// candidates.  This is exact: every key of the row's top k is in its
+// workgroup (when the row stride allows no longer rows).  Otherwise a row is
+// cut into nseg nearly equal segments of at most 8192 scores while the grid's
+// second dimension (which the caller's workspace and the merge's 16384
+// candidates bound) allows, else of at most 16384, each selected by its own
+// workgroup into k candidates (score, index) in the workspace; a second
+// launch then selects the row's top k among its nseg * k candidates.  This is exact: every key of the row's top k is in its
 // segment's top k under the same order (score descending, index ascending),
 // and for any one score a segment lists its keys in index order, so taking
 // equal candidates in list order still takes the lowest indices.  Only the
@@ -842,14 +843,13 @@ __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
       for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const int need = (n + kTopkSegmentKeys - 1) / kTopkSegmentKeys;
   const int grid = a.seg_grid;  // the launch grid's second dimension
-  if (grid > 1 && need > grid) return;  // selected whole by the merge launch
-  const int nseg = min(need, grid);
+  const int nseg = topk_row_segments(n, grid);
+  if (nseg == 0) return;  // selected whole by the merge launch
   if (s >= nseg) return;
   // a row of one segment selects straight into out_idx; otherwise nearly
-  // equal segments (each holds more than k scores: at least half a segment's
-  // worth, and k <= 2048) select k candidates each into the workspace
+  // equal segments (each holds more than k scores) select k candidates each
+  // into the workspace
   const int64_t s0 = (int64_t)n * s / nseg, s1 = (int64_t)n * (s + 1) / nseg;
   const int64_t slot = ((int64_t)r * grid + s) * k;
   const float* seg = a.logits + (int64_t)r * a.row_stride + s0;
@@ -915,13 +915,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
   const int r = blockIdx.x;
   const int n = row_len(ctx, r, next_n, row_stride);
   if (n <= k) return;
-  const int need = (n + kTopkSegmentKeys - 1) / kTopkSegmentKeys;
+  const int nseg = topk_row_segments(n, seg_grid);
   const SelectOut out{out_idx + (int64_t)r * k, nullptr, 0};
-  if (need > seg_grid) {
+  if (nseg == 0) {
     select_keys<true>(logits + (int64_t)r * row_stride, n, k, out, sh);
     return;
   }
-  const int nseg = need;
   if (nseg < 2) return;
   const int m = nseg * k;
   const int64_t slot = (int64_t)r * seg_grid * k;

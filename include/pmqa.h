@@ -170,12 +170,15 @@ PMQA_API pmqa_status paged_mqa_logits_preshuffled(const void* q, const void* kv_
  * workspace     DEVICE scratch owned by the caller, 16-byte aligned, or NULL
  *               when workspace_bytes is 0.  Its contents on entry are ignored
  *               and on return unspecified; calls that share it must be ordered
- *               on one stream.  A row longer than 16384 visible scores is split
- *               into segments, each selected by its own workgroup into k
- *               candidates held here, and a second launch merges them; the
- *               workspace bounds how far rows are split (the candidates of
- *               every row's segments must fit), never the result: a smaller
- *               one (0 included) only gives long rows fewer, longer segments.
+ *               on one stream.  When logits_row_stride exceeds 16384, a row
+ *               of more than 8192 visible scores is split into segments of at
+ *               most 8192 scores (of at most 16384 when the workspace or the
+ *               merge's 16384 candidates allow no more segments), each
+ *               selected by its own workgroup into k candidates held here, and
+ *               a second launch merges them; the workspace bounds how far rows
+ *               are split (the candidates of every row's segments must fit),
+ *               never the result: a smaller one (0 included) only gives long
+ *               rows fewer, longer segments.
  *               topk_per_row_workspace_size gives the size that splits rows of
  *               up to a given length fully.
  * workspace_bytes  bytes at workspace.  PMQA_ERR_WORKSPACE when it is nonzero
@@ -205,7 +208,7 @@ PMQA_API pmqa_status topk_per_row(const float* logits, const int32_t* context_le
  * first call on a device looks up that device's copy (hipGetSymbolAddress);
  * a failure there returns PMQA_ERR_HIP.
  */
-#define PMQA_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define PMQA_NOALLOC_SCRATCH_BYTES (64u << 20)
 PMQA_API pmqa_status topk_per_row_noalloc(const float* logits, const int32_t* context_lens,
                                           int32_t k, int32_t* out_idx, int32_t batch,
                                           int32_t next_n, int64_t logits_row_stride,
@@ -214,8 +217,9 @@ PMQA_API pmqa_status topk_per_row_noalloc(const float* logits, const int32_t* co
 /*
  * topk_per_row_workspace_size - workspace bytes with which topk_per_row splits
  * every row of up to max_row_len visible scores as far as it splits rows
- * (segments of at most 16384 scores, at most 16384 / k of them): rows * k * 8
- * bytes per segment of the longest row, 0 when no row that long is split.
+ * (segments of at most 8192 scores, at most 16384 / k of them): rows * k * 8
+ * bytes per segment of the longest row; 0 when max_row_len <= 16384 (rows that
+ * short are never split).
  * Host only.  Returns 0 for invalid arguments (rows < 0, k outside 1..2048,
  * max_row_len < 0).
  */

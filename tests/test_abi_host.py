@@ -101,12 +101,12 @@ def test_topk_host_checks(lib, kw, status):
 @pytest.mark.parametrize("rows,k,max_len,want", [
     (64, 2048, 8192, 0),            # rows of one segment are never split
     (64, 2048, 16384, 0),
-    (64, 2048, 16385, 64 * 2 * 2048 * 8),
+    (64, 2048, 16385, 64 * 3 * 2048 * 8),     # longer rows: segments of <= 8192
     (64, 2048, 131072, 64 * 8 * 2048 * 8),
     (64, 2048, 1 << 20, 64 * 8 * 2048 * 8),   # the merge holds 8 segments of 2048
-    (1024, 2048, 32768, 1024 * 2 * 2048 * 8),
-    (5, 100, 1 << 20, 5 * 64 * 100 * 8),      # 64 segments of 16384; 6400 candidates
-    (5, 1, 1 << 20, 5 * 64 * 1 * 8),
+    (1024, 2048, 32768, 1024 * 4 * 2048 * 8),
+    (5, 100, 1 << 20, 5 * 128 * 100 * 8),     # 128 segments of 8192; 12800 candidates
+    (5, 1, 1 << 20, 5 * 128 * 1 * 8),
     (0, 16, 1 << 20, 0),
     (-1, 16, 100000, 0), (4, 0, 100000, 0), (4, 2049, 100000, 0), (4, 16, -1, 0),
 ])
@@ -205,7 +205,7 @@ def noalloc(lib, **kw):
     (dict(lg=None), ERR_NULL), (dict(ctx=None), ERR_NULL), (dict(out=None), ERR_NULL),
     (dict(k=0), ERR_SHAPE), (dict(nn=0), ERR_SHAPE), (dict(rs=0), ERR_SHAPE), (dict(b=-1), ERR_SHAPE),
     # the split the stride calls for needs more than the library's scratch:
-    # 1024 rows * 8 segments * 2048 candidates * 8 bytes = 128 MiB > 32 MiB
+    # 1024 rows * 8 segments * 2048 candidates * 8 bytes = 128 MiB > 64 MiB
     (dict(b=1024, rs=1 << 20), ERR_WORKSPACE), (dict(b=1024, rs=1 << 20, lg=None), ERR_WORKSPACE),
     (dict(b=0), OK), (dict(b=0, lg=None), OK),
 ])
@@ -216,10 +216,11 @@ def test_topk_noalloc_host_checks(lib, kw, status):
 def test_noalloc_scratch_size_in_header_matches_a_full_split():
     text = open(os.path.join(ROOT, "include", "pmqa.h")).read()
     m = re.search(r"#define PMQA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
-    assert m and int(m.group(1)) << int(m.group(2)) == 32 << 20
-    # the long-context workload's full split fits; the MTP workload's stride does not
-    assert pm.topk_workspace_size(64, 2048, 131072) <= 32 << 20
-    assert pm.topk_workspace_size(1024, 2048, 1 << 20) > 32 << 20
+    assert m and int(m.group(1)) << int(m.group(2)) == 64 << 20
+    # the long-context and small-pages workloads' full splits fit; the MTP workload's stride does not
+    assert pm.topk_workspace_size(64, 2048, 131072) <= 64 << 20
+    assert pm.topk_workspace_size(384, 2048, 65536) <= 64 << 20
+    assert pm.topk_workspace_size(1024, 2048, 1 << 20) > 64 << 20
 
 
 @pytest.mark.parametrize("ps,status", [(1, ERR_UNSUPPORTED), (2, ERR_UNSUPPORTED),

@@ -627,13 +627,15 @@ def _topk_exact(gpu_lib, dense, lens, k, workspace, label):
 
 @pytest.mark.parametrize("ties", [0, 3])
 def test_topk_segments_and_workspace_sizes(gpu_lib, ties):
-    """Rows longer than one segment (16384 scores) are split over workgroups
-    into candidates in the workspace, then merged: exact sets for every
-    workspace size (none: one workgroup per row, streamed; room for 3
+    """Rows longer than one segment are split over workgroups into candidates
+    in the workspace (segments of at most 8192 scores while the grid has
+    room, else of at most 16384), then merged: exact sets for every
+    workspace size (none: one workgroup per row, streamed; room for a few
     segments; the full split), with many equal scores at the k-th boundary
     spread over segments (lowest indices win), at lengths on both sides of
-    the segment multiples."""
-    lens = [16383, 16384, 16385, 20000, 32768, 32769, 50000, 65536, 98304, 131072, 200000, 5]
+    the segment multiples and of the switch to longer segments."""
+    lens = [16383, 16384, 16385, 20000, 32768, 32769, 50000, 65536, 98304, 131072, 200000, 5,
+            8193, 24577, 65537]
     width = max(lens)
     dense = synth.make_logit_rows(len(lens), width, lens, seed=9, ties=ties)
     rows = len(lens)

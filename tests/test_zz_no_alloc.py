@@ -41,7 +41,7 @@ def test_noalloc_matches_topk_per_row_twice(gpu_lib):
         logits = torch.from_numpy(dense).cuda()
         ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
         need = gpu_lib.topk_workspace_size(len(lens), k, width)
-        assert 0 < need <= 32 << 20
+        assert 0 < need <= 64 << 20
         ref = torch.full((len(lens), k), -7, dtype=torch.int32, device="cuda")
         ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         say(f"[gpu] topk_per_row rows={len(lens)} width={width} k={k} workspace={need}")
@@ -62,7 +62,7 @@ def test_noalloc_matches_topk_per_row_twice(gpu_lib):
 def test_noalloc_refuses_a_split_beyond_the_scratch(gpu_lib):
     lib = gpu_lib.load_library()
     rows, k, stride = 1024, 2048, 1 << 20
-    assert gpu_lib.topk_workspace_size(rows, k, stride) > 32 << 20
+    assert gpu_lib.topk_workspace_size(rows, k, stride) > 64 << 20
     # a buffer of the stride claimed (nothing may be read from it, but a launch
     # would still stay inside it)
     logits = torch.empty((rows, stride), dtype=torch.float32, device="cuda")
