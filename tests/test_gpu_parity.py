@@ -672,3 +672,28 @@ def test_topk_merge_graph_replay(gpu_lib):
         torch.cuda.synchronize()
         assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), np.sort(eager, axis=1))
         _topk_exact(gpu_lib, dense, lens, k, ws, "eager between replays")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_topk_random_shapes(gpu_lib, seed):
+    """Random batches of rows (lengths from 0 to past the split thresholds,
+    a few with many ties), random k, stride and workspace size (none, part of
+    a full split, a full split): exact sets against the oracle every time."""
+    rng = np.random.default_rng(1000 + seed)
+    for trial in range(4):
+        rows = int(rng.integers(1, 40))
+        k = int(rng.choice([1, 3, 64, 100, 500, 1024, 2047, 2048]))
+        cls = rng.integers(0, 4, rows)
+        lens = np.where(cls == 0, rng.integers(0, 3000, rows),
+                        np.where(cls == 1, rng.integers(3000, 16385, rows),
+                                 np.where(cls == 2, rng.integers(16385, 70000, rows),
+                                          rng.integers(0, 2 * k + 2, rows)))).astype(np.int64)
+        stride = int(max(1, lens.max()) + rng.integers(0, 300))
+        dense = synth.make_logit_rows(rows, stride, lens.tolist(), seed=int(rng.integers(1 << 30)),
+                                      ties=int(rng.choice([0, 0, 4])))
+        full = gpu_lib.topk_workspace_size(rows, k, stride)
+        nbytes = int(rng.choice([0, full // 3, full])) if full else 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        say(f"[gpu] top-k random shapes seed={seed} trial={trial} rows={rows} k={k} "
+            f"stride={stride} workspace={nbytes}/{full}")
+        _topk_exact(gpu_lib, dense, lens.tolist(), k, ws, f"random seed={seed} trial={trial}")
