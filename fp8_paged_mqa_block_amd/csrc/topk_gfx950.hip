@@ -17,16 +17,18 @@
 // visible scores [0, visible) are read.
 //
 // A list held in registers (up to 16384 scores, 16 a thread) is first tried
-// in one pass on the floats themselves (select_held): value buckets between
-// its smallest and largest score, the threshold bucket, then every score
-// above it staged in LDS at its slot and the threshold bucket's few scores
-// ranked directly.  One CU issues every instruction of a row, so this path
-// keeps a fixed, small number of instructions per score (no per-score
-// branches or ballots).  Lists it cannot resolve that way (a non-finite
-// score, all scores equal, a crowded threshold bucket), longer rows, and in
-// the split grid lists of more than 8192 scores (whose floats and buckets
-// would exceed the register budget of two workgroups per CU) take the radix
-// passes below.
+// on the floats themselves (select_held): value buckets between its smallest
+// and largest score, the threshold bucket (split again into value buckets,
+// up to three passes in all, while it holds too many scores: heavy-tailed
+// rows crowd the lowest buckets), then every score above it staged in LDS at
+// its slot and the threshold bucket's few scores ranked directly.  One CU
+// issues every instruction of a row, so this path keeps a fixed, small
+// number of instructions per score and pass (no per-score branches or
+// ballots).  Lists it cannot resolve that way (a non-finite score, all
+// scores equal, a threshold bucket still crowded after three passes), longer
+// rows, and in the two-per-CU split grid lists of more than 8192 scores
+// (whose floats and buckets would exceed its register budget) take the
+// radix passes below.
 //
 // One workgroup's exact select on order-preserving 32-bit keys keeps every
 // step off long LDS round-trip chains, which dominate at these sizes:
@@ -77,6 +79,7 @@ constexpr int kSmallKeys = 8;           // keys per thread for rows up to 8192
 constexpr int kLargeKeys = 16;          // keys per thread (or per chunk) beyond
 constexpr int kCandCap = 256;           // threshold bins this small are ranked directly
 constexpr int kCandCapHeld = 128;       // the same, for rows held in registers
+constexpr int kHeldPasses = 3;          // value-bucket passes over scores held as floats
 // Third word of a raw buffer resource on gfx9-family chips (gfx950): 32-bit
 // elements, bounds checked against the record count in bytes.
 constexpr int kBufferFlags = 0x00020000;
@@ -326,12 +329,15 @@ struct Held {
   }
 };
 
-// The top k of n > k scores held as floats, in one bucket pass: value buckets
-// between the smallest and largest score (Buckets), the threshold bucket found
-// from the histogram, then every score above it placed and the threshold
-// bucket's scores ranked against each other.  Every phase is a fixed number of
-// instructions per held score, with no per-score branches or ballots (the
-// costs that dominated: one CU issues the whole row's instructions):
+// The top k of n > k scores held as floats, by value buckets: buckets between
+// the smallest and largest score (Buckets), the threshold bucket found from
+// the histogram and, while it holds more than 128 scores that are not all
+// taken, its value range cut into buckets again (at most kHeldPasses passes;
+// each cut is monotone in the score too), then every score above it placed
+// and the threshold bucket's scores ranked against each other.  Every phase
+// is a fixed number of instructions per held score, with no per-score
+// branches or ballots (the costs that dominated: one CU issues the whole
+// row's instructions):
 //  * positions past the list get a negative bucket, which the histogram
 //    counts in an extra bin per lane and every comparison (signed) puts below
 //    all buckets;
@@ -344,7 +350,8 @@ struct Held {
 //    take the lowest indices.
 // Returns false, having written nothing, when the row needs radix passes: a
 // non-finite score, all scores equal, or more than 128 scores in a threshold
-// bucket it cannot take whole.  The output is deterministic.
+// bucket it cannot take whole after the last pass (or whose range is too
+// narrow to cut).  The output is deterministic.
 template <int KPT, bool IDX, bool VALS>
 __device__ __forceinline__ bool select_held(int n, int k, const SelectOut& out, TopkShared& sh,
                                             const Held<KPT, IDX>& hd) {
@@ -388,56 +395,87 @@ __device__ __forceinline__ bool select_held(int n, int k, const SelectOut& out, 
     return false;
   }
 
-  // ---- buckets and their histogram ----
-  const float off = -bk.lo * bk.scale;
+  // ---- buckets, refined until the bucket of the k-th score is small ----
+  // kb[j]: the score's bucket among the current candidates (pass 0: every
+  // score), kAbove / kBelow once an earlier pass put it above / below them
+  // (positions past the list start below); signed comparisons order all three
+  constexpr uint32_t kAbove = 0x7FFFFFFFu, kBelow = ~0u;
+  float lo = bk.lo, scale = bk.scale;
+  float off = -lo * scale;
   uint32_t kb[KPT];
   auto bucket_all = [&](auto all) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      kb[j] = decltype(all)::value || tb + j < n ? bk.of_value(hd.x[j], off) : ~0u;
+      kb[j] = decltype(all)::value || tb + j < n ? bk.of_value(hd.x[j], off) : kBelow;
   };
   if (full) bucket_all(std::true_type{});
   else bucket_all(std::false_type{});
-  uint32_t* h = sh.hist[0];
   const uint32_t spare = (uint32_t)(kBins + lane);
+  uint32_t above = 0;              // scores above the candidates, from earlier passes
+  uint32_t need = (uint32_t)k;     // rank of the k-th score among the candidates
+  uint32_t bs, first_eq, cnt, remaining;
+  for (int pass = 0;; ++pass) {
+    uint32_t* h = sh.hist[pass & 1];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) atomicAdd(&h[min(kb[j], spare)], 1u);
-  __syncthreads();
-
-  // ---- the bucket holding the k-th score ----
-  const uint2 mine = reinterpret_cast<const uint2*>(h)[tid];  // buckets 2*tid, 2*tid+1
-  const uint32_t wtot = wave_sum(mine.x + mine.y);
-  if (lane == 0) sh.part[wave] = wtot;
-  __syncthreads();
-  const uint32_t pv = sh.part[lane & 15];
-  const uint32_t pw = row_prefix(pv);
-  const uint32_t t16 = lane_of(pw, 15);
-  const uint32_t above_w = t16 - pw;  // scores in higher wave spans
-  const uint64_t fw = __ballot(lane < 16 && above_w < (uint32_t)k && above_w + pv >= (uint32_t)k);
-  const int ws = min((int)__builtin_ctzll(fw), kWaves - 1);
-  const uint32_t base_above = lane_of(above_w, ws);
-  const uint2 hb = reinterpret_cast<const uint2*>(h)[ws * 64 + lane];
-  const uint32_t s2 = hb.x + hb.y;
-  uint32_t t_w;
-  const uint32_t ps = wave_prefix(s2, lane, t_w);
-  const uint32_t above_l = base_above + (t_w - ps);
-  const uint64_t fl = __ballot(above_l < (uint32_t)k && above_l + s2 >= (uint32_t)k);
-  const int ls = min((int)__builtin_ctzll(fl), 63);
-  const uint32_t a = lane_of(above_l, ls);
-  const uint32_t h0 = lane_of(hb.x, ls), h1 = lane_of(hb.y, ls);
-  const uint32_t bin_hi = 2u * (uint32_t)(ws * 64 + ls) + 1u;
-  uint32_t bs, first_eq, cnt;
-  if (a + h1 >= (uint32_t)k) {
-    bs = bin_hi; first_eq = a; cnt = h1;
-  } else {
-    bs = bin_hi - 1u; first_eq = a + h1; cnt = h0;
-  }
-  const uint32_t remaining = (uint32_t)k - first_eq;  // taken from the threshold bucket
-  const bool whole = cnt == remaining;
-  if (!whole && cnt > (uint32_t)kCandCapHeld) {
+    for (int j = 0; j < KPT; ++j) atomicAdd(&h[min(kb[j], spare)], 1u);
     __syncthreads();
-    return false;
+    // the other buffer, for a next pass (its last reads, two passes back,
+    // are behind the barrier above)
+    reinterpret_cast<uint2*>(sh.hist[(pass & 1) ^ 1])[tid] = uint2{0u, 0u};
+
+    // ---- the bucket holding the need-th candidate ----
+    const uint2 mine = reinterpret_cast<const uint2*>(h)[tid];  // buckets 2*tid, 2*tid+1
+    const uint32_t wtot = wave_sum(mine.x + mine.y);
+    if (lane == 0) sh.part[wave] = wtot;
+    __syncthreads();
+    const uint32_t pv = sh.part[lane & 15];
+    const uint32_t pw = row_prefix(pv);
+    const uint32_t t16 = lane_of(pw, 15);
+    const uint32_t above_w = t16 - pw;  // candidates in higher wave spans
+    const uint64_t fw = __ballot(lane < 16 && above_w < need && above_w + pv >= need);
+    const int ws = min((int)__builtin_ctzll(fw), kWaves - 1);
+    const uint32_t base_above = lane_of(above_w, ws);
+    const uint2 hb = reinterpret_cast<const uint2*>(h)[ws * 64 + lane];
+    const uint32_t s2 = hb.x + hb.y;
+    uint32_t t_w;
+    const uint32_t ps = wave_prefix(s2, lane, t_w);
+    const uint32_t above_l = base_above + (t_w - ps);
+    const uint64_t fl = __ballot(above_l < need && above_l + s2 >= need);
+    const int ls = min((int)__builtin_ctzll(fl), 63);
+    const uint32_t a = lane_of(above_l, ls);
+    const uint32_t h0 = lane_of(hb.x, ls), h1 = lane_of(hb.y, ls);
+    const uint32_t bin_hi = 2u * (uint32_t)(ws * 64 + ls) + 1u;
+    uint32_t fe;
+    if (a + h1 >= need) {
+      bs = bin_hi; fe = a; cnt = h1;
+    } else {
+      bs = bin_hi - 1u; fe = a + h1; cnt = h0;
+    }
+    remaining = need - fe;  // taken from the threshold bucket
+    first_eq = above + fe;
+    if (cnt == remaining || cnt <= (uint32_t)kCandCapHeld) break;
+    // too many candidates share the bucket: the next pass splits that
+    // bucket's value range into kBins buckets (again monotone in the score,
+    // the clamp included, so still exact), the other scores settled
+    const float lo2 = lo + (float)bs / scale;
+    const float scale2 = scale * (float)kBins;
+    if (pass + 1 == kHeldPasses || !(scale2 <= 3.0e38f)) {
+      __syncthreads();  // the radix passes reuse what was read above
+      return false;
+    }
+    const float off2 = -lo2 * scale2;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t sub = (uint32_t)(int)__builtin_amdgcn_fmed3f(
+          __builtin_fmaf(hd.x[j], scale2, off2), 0.f, (float)(kBins - 1));
+      kb[j] = kb[j] == bs ? sub : ((int)kb[j] > (int)bs ? kAbove : kBelow);
+    }
+    above = first_eq;
+    need = remaining;
+    lo = lo2;
+    scale = scale2;
   }
+  const bool whole = cnt == remaining;
 
   // ---- each score's slot: above the bucket [0, first_eq), in it after ----
   uint32_t ca = 0, ce = 0;
@@ -830,8 +868,9 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ row, int n
 // the grid has is left to the merge launch, which selects it whole, so the
 // stage keeps only the register-resident layouts.  SPLIT: the grid may split
 // rows (its segments stage their candidates' scores); otherwise every row
-// is one segment and only indices are staged.
-template <bool STREAM, bool SPLIT>
+// is one segment and only indices are staged.  WIDE (split grids): segments
+// of more than 8192 scores also take the one-pass select on floats.
+template <bool STREAM, bool SPLIT, bool WIDE = false>
 __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
   const int r = blockIdx.x;
   const int s = blockIdx.y;
@@ -858,7 +897,7 @@ __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
     // workgroups per CU): a row of one segment stages values it never stores
     const SelectOut so = nseg == 1 ? SelectOut{out, nullptr, 0}
                                    : SelectOut{a.cand_idx + slot, a.cand_val + slot, (int32_t)s0};
-    select_keys<false, false, true>(seg, (int)(s1 - s0), k, so, sh);
+    select_keys<false, WIDE, true>(seg, (int)(s1 - s0), k, so, sh);
   } else {
     select_keys<STREAM, true, false>(seg, n, k, SelectOut{out, nullptr, 0}, sh);
   }
@@ -900,34 +939,85 @@ void topk_split_kernel(const float* __restrict__ logits, int64_t row_stride,
                       sh);
 }
 
+// Stage 1 for split grids whose segments may hold more than 8192 scores
+// (rows longer than 8192 times the grid's segments): such segments take the
+// one-pass select on 16 floats a thread, which leaves room for one
+// workgroup per CU, instead of the radix passes (measured on 65K-131K-score
+// rows in 8 segments: a segment's workgroup took 11-25 us in the radix
+// passes).
+__global__ __launch_bounds__(kThreads) void topk_split_wide_kernel(
+    const float* __restrict__ logits, int64_t row_stride, const int32_t* __restrict__ ctx,
+    int32_t next_n, int32_t k, int32_t seg_grid, int32_t* __restrict__ out_idx,
+    float* __restrict__ cand_val, int32_t* __restrict__ cand_idx) {
+  __shared__ TopkShared sh;
+  stage1<false, true, true>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val,
+                                     cand_idx, seg_grid},
+                            sh);
+}
+
 // Stage 2 (launched when the grid has more than one segment per row).
 // Workgroup r selects the top k of row r among its segments' nseg * k
 // candidates (at most kTopkMergeKeys: the host caps the segments), held in
 // registers with their indices; or, for a row longer than the grid's
 // segments can hold, the whole row, streamed.  Rows of one segment or none
-// were finished in stage 1.
+// were finished in stage 1.  SMALL (seg_grid * k <= 8192, so every row has
+// at most 8192 candidates): only the 8-a-thread layouts are compiled, a row
+// left whole streamed 8 keys a thread at a time, so that the registers leave
+// room for two workgroups per CU.
+template <bool SMALL>
+__device__ __forceinline__ void merge_row(const TopkArgs& a, TopkShared& sh) {
+  const int r = blockIdx.x;
+  const int n = row_len(a.ctx, r, a.next_n, a.row_stride);
+  const int k = a.k;
+  if (n <= k) return;
+  const int nseg = topk_row_segments(n, a.seg_grid);
+  const SelectOut out{a.out_idx + (int64_t)r * k, nullptr, 0};
+  if (nseg == 0) {
+    const float* row = a.logits + (int64_t)r * a.row_stride;
+    if constexpr (SMALL) {
+      // streamed 8 keys a thread at a time (the registers of this kernel)
+      const int tb = (int)(threadIdx.x >> 6) * 64 * kSmallKeys + (int)(threadIdx.x & 63);
+      Chunk<kSmallKeys> ch;
+      ch.load(row, n, 0, tb);
+      select_row<kSmallKeys, true>(row, n, k, out, sh, ch);
+    } else {
+      select_keys<true>(row, n, k, out, sh);
+    }
+    return;
+  }
+  if (nseg < 2) return;
+  const int m = nseg * k;
+  const int64_t slot = (int64_t)r * a.seg_grid * k;
+  const float* cv = a.cand_val + slot;
+  const int32_t* ci = a.cand_idx + slot;
+  if (m <= kThreads * kSmallKeys) {
+    held_or_radix<kSmallKeys, true, false>(cv, ci, m, k, out, sh);
+  } else if constexpr (!SMALL) {
+    held_or_radix<kLargeKeys, true, false>(cv, ci, m, k, out, sh);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     const float* __restrict__ logits, int64_t row_stride, const int32_t* __restrict__ ctx,
     int32_t next_n, int32_t k, int32_t seg_grid, int32_t* __restrict__ out_idx,
     float* __restrict__ cand_val, int32_t* __restrict__ cand_idx) {
   __shared__ TopkShared sh;
+  merge_row<false>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val, cand_idx,
+                            seg_grid},
+                   sh);
+}
 
-  const int r = blockIdx.x;
-  const int n = row_len(ctx, r, next_n, row_stride);
-  if (n <= k) return;
-  const int nseg = topk_row_segments(n, seg_grid);
-  const SelectOut out{out_idx + (int64_t)r * k, nullptr, 0};
-  if (nseg == 0) {
-    select_keys<true>(logits + (int64_t)r * row_stride, n, k, out, sh);
-    return;
-  }
-  if (nseg < 2) return;
-  const int m = nseg * k;
-  const int64_t slot = (int64_t)r * seg_grid * k;
-  const float* cv = cand_val + slot;
-  const int32_t* ci = cand_idx + slot;
-  if (m <= kThreads * kSmallKeys) held_or_radix<kSmallKeys, true, false>(cv, ci, m, k, out, sh);
-  else held_or_radix<kLargeKeys, true, false>(cv, ci, m, k, out, sh);
+// The merge of grids whose rows have at most 8192 candidates each, held to
+// 80 SGPRs as the split stage is, so that two workgroups share a CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(80), amdgpu_waves_per_eu(8)))
+void topk_merge_small_kernel(const float* __restrict__ logits, int64_t row_stride,
+                             const int32_t* __restrict__ ctx, int32_t next_n, int32_t k,
+                             int32_t seg_grid, int32_t* __restrict__ out_idx,
+                             float* __restrict__ cand_val, int32_t* __restrict__ cand_idx) {
+  __shared__ TopkShared sh;
+  merge_row<true>(TopkArgs{logits, row_stride, ctx, next_n, k, out_idx, cand_val, cand_idx,
+                           seg_grid},
+                  sh);
 }
 
 }  // namespace
@@ -971,7 +1061,21 @@ hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t 
   // the merge launch takes them
   const int64_t longest = p.row_stride < INT32_MAX ? p.row_stride : INT32_MAX;
   const bool stream_keys = !merge && longest > kTopkSegmentKeys;
-  auto kern = merge ? topk_split_kernel : (stream_keys ? topk_kernel<true> : topk_kernel<false>);
+  // Which split-stage kernel (both select any segment exactly): segments of
+  // more than 8192 scores come from rows longer than 8192 per segment of the
+  // grid.  A grid narrower than the merge allows was bounded by the caller's
+  // workspace, sized for the caller's longest row, so its segments are
+  // expected to hold at most 8192 scores (the two-per-CU kernel); a grid at
+  // the merge's limit on rows whose stride allows longer segments takes the
+  // kernel that holds 16 floats a thread.
+  const int64_t merge_cap = kTopkMergeKeys / p.k;
+  const bool wide = merge && p.seg_grid >= merge_cap &&
+                    (longest + kTopkSplitKeys - 1) / kTopkSplitKeys > p.seg_grid;
+  // a merge of at most 8192 candidates a row fits two workgroups per CU
+  const bool small_merge = (int64_t)p.seg_grid * p.k <= kThreads * kSmallKeys;
+  auto kern = merge ? (wide ? topk_split_wide_kernel : topk_split_kernel)
+                    : (stream_keys ? topk_kernel<true> : topk_kernel<false>);
+  auto merge_kern = small_merge ? topk_merge_small_kernel : topk_merge_kernel;
   if (tm.start || tm.stop)
     hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, tm.start,
                           merge ? nullptr : tm.stop, 0, p.logits, p.row_stride, p.ctx, p.next_n,
@@ -983,11 +1087,11 @@ hipError_t launch_topk(const TopkParams& p, const LaunchTiming& tm, hipStream_t 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (tm.start || tm.stop)
-      hipExtLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(kThreads), 0, stream, nullptr,
+      hipExtLaunchKernelGGL(merge_kern, dim3(rows), dim3(kThreads), 0, stream, nullptr,
                             tm.stop, 0, p.logits, p.row_stride, p.ctx, p.next_n, p.k, p.seg_grid,
                             p.out_idx, p.cand_val, p.cand_idx);
     else
-      hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(kThreads), 0, stream, p.logits,
+      hipLaunchKernelGGL(merge_kern, dim3(rows), dim3(kThreads), 0, stream, p.logits,
                          p.row_stride, p.ctx, p.next_n, p.k, p.seg_grid, p.out_idx, p.cand_val,
                          p.cand_idx);
   }

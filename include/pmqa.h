@@ -180,7 +180,10 @@ PMQA_API pmqa_status paged_mqa_logits_preshuffled(const void* q, const void* kv_
  *               never the result: a smaller one (0 included) only gives long
  *               rows fewer, longer segments.
  *               topk_per_row_workspace_size gives the size that splits rows of
- *               up to a given length fully.
+ *               up to a given length fully; sized for the longest visible row
+ *               (rather than for the stride) it is also what lets the split
+ *               launch assume segments of at most 8192 scores and run two
+ *               workgroups per CU.
  * workspace_bytes  bytes at workspace.  PMQA_ERR_WORKSPACE when it is nonzero
  *               and workspace is NULL.
  * stream        hipStream_t to enqueue on.

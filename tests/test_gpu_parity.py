@@ -267,12 +267,15 @@ def test_topk_special_rows(gpu_lib, split):
     repeated (every key ties), both zeros (equal scores), infinities, subnormals
     and both signs, extremes whose difference overflows, a heavy tail, values a
     few ulps apart, at lengths on each side of the register-resident limits.
-    With a full workspace the 40000-score rows are split (and the shorter rows
-    go through the split grid); with none, every row is one workgroup's, the
-    shorter rows through the one-pass select on floats and its fallbacks."""
+    With a full workspace the 40000- and 100000-score rows are split (and the
+    shorter rows go through the split grid: at k = 2048 the grid that holds
+    16 floats a thread, whose 100000-score rows have segments of 12500; at
+    smaller k the two-per-CU grid and merge); with none, every row is one
+    workgroup's, the shorter rows through the one-pass select on floats and
+    its fallbacks."""
     rng = np.random.default_rng(11)
     rows = []
-    for n in (3000, 9000, 40000):
+    for n in (3000, 9000, 40000, 100000):
         rows.append(np.full(n, 1.5, dtype=np.float32))
         z = np.where(rng.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
         z[rng.choice(n, 50, replace=False)] = 1.0
