@@ -680,8 +680,11 @@ def test_topk_merge_graph_replay(gpu_lib):
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_topk_random_shapes(gpu_lib, seed):
     """Random batches of rows (lengths from 0 to past the split thresholds,
-    a few with many ties), random k, stride and workspace size (none, part of
-    a full split, a full split): exact sets against the oracle every time."""
+    a few with many ties; bell-shaped, one-sided or two-sided heavy-tailed
+    scores, the tails crowding a few value buckets so that the select cuts
+    them again or falls back), random k, stride and workspace size (none, part
+    of a full split, a full split): exact sets against the oracle every
+    time."""
     rng = np.random.default_rng(1000 + seed)
     for trial in range(4):
         rows = int(rng.integers(1, 40))
@@ -694,9 +697,14 @@ def test_topk_random_shapes(gpu_lib, seed):
         stride = int(max(1, lens.max()) + rng.integers(0, 300))
         dense = synth.make_logit_rows(rows, stride, lens.tolist(), seed=int(rng.integers(1 << 30)),
                                       ties=int(rng.choice([0, 0, 4])))
+        tail = int(rng.integers(0, 3))
+        if tail == 1:    # one-sided heavy tail (positions past a row are never read)
+            dense = np.exp(dense.astype(np.float64) * 4.0).astype(np.float32)
+        elif tail == 2:  # heavy tails on both sides
+            dense = np.sinh(dense.astype(np.float64) * 4.0).astype(np.float32)
         full = gpu_lib.topk_workspace_size(rows, k, stride)
         nbytes = int(rng.choice([0, full // 3, full])) if full else 0
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         say(f"[gpu] top-k random shapes seed={seed} trial={trial} rows={rows} k={k} "
-            f"stride={stride} workspace={nbytes}/{full}")
+            f"stride={stride} workspace={nbytes}/{full} tail={tail}")
         _topk_exact(gpu_lib, dense, lens.tolist(), k, ws, f"random seed={seed} trial={trial}")
