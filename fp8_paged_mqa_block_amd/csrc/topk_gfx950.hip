@@ -10,11 +10,14 @@
 // second dimension (which the caller's workspace and the merge's 16384
 // candidates bound) allows, else of at most 16384, each selected by its own
 // workgroup into k candidates (score, index) in the workspace; a second
-// launch then selects the row's top k among its nseg * k candidates.  This is exact: every key of the row's top k is in its
-// segment's top k under the same order (score descending, index ascending),
-// and for any one score a segment lists its keys in index order, so taking
-// equal candidates in list order still takes the lowest indices.  Only the
-// visible scores [0, visible) are read.
+// launch then selects the row's top k among its nseg * k candidates.  This is
+// exact: every key of the row's top k is in its segment's top k under the
+// same order (score descending, index ascending), and for any one score a
+// segment lists its keys in index order, so taking equal candidates in list
+// order still takes the lowest indices.  Only the visible scores
+// [0, visible) are read.  Each launch has two kernels that differ only in
+// their register layouts (two workgroups per CU, or 16 floats a thread at
+// one per CU); the host picks them from the grid (launch_topk).
 //
 // A list held in registers (up to 16384 scores, 16 a thread) is first tried
 // on the floats themselves (select_held): value buckets between its smallest
