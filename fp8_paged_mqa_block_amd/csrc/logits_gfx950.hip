@@ -690,23 +690,24 @@ __device__ __forceinline__ void score_iteration(const LogitsParams& p, const Run
       }
       part[jj][tile] = sum;
     }
-    if constexpr (FACTORED && !EXACT) {
-      // Each matrix product is read by 8 vector instructions (4 relu, 4 fma).
-      // Left to itself the scheduler reuses one result register set, so each
-      // product's reads wait out its latency (an 11-cycle nop per product)
-      // and the wave's matrix and vector work alternate.  This order keeps
-      // two products in flight: product g + 2 issues before the reads of
-      // product g, which then find it done (measured, interleaved: MTP
-      // 332 -> 304 us, long context 121 -> 114 us, decode 10.5 -> 9.9 us; a
-      // third product in flight measured the same).
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 matrix products
+  }
+  if constexpr (FACTORED && !EXACT) {
+    // Each matrix product is read by 8 vector instructions (4 relu, 4 fma).
+    // Left to itself the scheduler reuses one result register set, so each
+    // product's reads wait out its latency (an 11-cycle nop per product) and
+    // the wave's matrix and vector work alternate.  This order keeps two
+    // products in flight across the iteration's tiles: product g + 2 issues
+    // before the reads of product g, which then find it done (measured,
+    // interleaved on one box: MTP 307 -> 293 us, long context 113 -> 110 us;
+    // per tile instead of per iteration 300 and 111 us; a third product in
+    // flight no better).
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 matrix products
 #pragma unroll
-      for (int g = 0; g < HT * JW - 2; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // 8 vector instructions
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // the next product
-      }
-      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+    for (int g = 0; g < kTilesPerIter * HT * JW - 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // 8 vector instructions
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // the next product
     }
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
   }
   // this lane's row kq ends with tile kq's tokens: its scale multiplies the
   // head-weighted sum in the factored form
