@@ -1312,10 +1312,11 @@ void logits_flat_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch, int
 // shape, a second slot per wave made waves stall on issuing its gather behind
 // the saturated memory pipeline before scoring the first, which cost more than
 // the prefetch gained.  Units of 128 q rows fit two waves per SIMD (8 per
-// workgroup, 2 iterations in flight each): on gfx950 a wave's own matrix and
-// vector instructions barely overlap, so a second wave per SIMD is what keeps
-// the matrix core busy (measured faster than 2 rows per wave at 1 wave per
-// SIMD, despite gathering each page once per row group).  Units of 192 rows
+// workgroup, 2 iterations in flight each): a second wave per SIMD is what
+// keeps the matrix core busy (measured faster than 2 rows per wave at 1 wave
+// per SIMD, despite gathering each page once per row group; measured before
+// the epilogue's schedule kept two products in flight, when a wave's own
+// matrix and vector instructions barely overlapped).  Units of 192 rows
 // also run two waves per SIMD: they then fill the 256 registers a wave gets
 // there (a few values spill, outside the scoring loop) and were measured about
 // 9% faster than one wave per SIMD with 4 iterations in flight.  Larger units
