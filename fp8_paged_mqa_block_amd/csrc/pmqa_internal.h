@@ -74,7 +74,7 @@ constexpr int kTopkMaxK = 2048;
 constexpr int kTopkSegmentKeys = 16384;
 constexpr int kTopkMergeKeys = 16384;
 // Scores a segment of a split row holds when the grid has room: 8 a thread,
-// the layout the one-pass select keeps within the register budget of two
+// the layout the value-bucket select keeps within the register budget of two
 // workgroups per CU.
 constexpr int kTopkSplitKeys = 8192;
 

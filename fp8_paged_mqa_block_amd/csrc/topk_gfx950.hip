@@ -813,7 +813,7 @@ __device__ __forceinline__ int row_len(const int32_t* __restrict__ ctx_lens, int
 }
 
 // Selects n > k scores held in registers (with IDX, candidates with their
-// row indices at `ids`): one bucket pass when that resolves the row, else the
+// row indices at `ids`): value-bucket passes when they resolve the row, else the
 // radix passes over the same scores as keys.  VALS: `out` takes the selected
 // scores too (a segment's candidates), else only their indices.
 template <int KPT, bool IDX, bool VALS>
@@ -839,7 +839,7 @@ __device__ __forceinline__ void held_or_radix(const float* __restrict__ vals,
 // Selects n keys at `row` (positions 0..n-1) into `out`, with the register
 // layout their count calls for.  Without STREAM the caller guarantees n <=
 // kTopkSegmentKeys (the keys fit the registers).  Without WIDE_HELD, lists of
-// more than 8192 keys skip the one-pass select on floats (its 16 floats and
+// more than 8192 keys skip the value-bucket select on floats (its 16 floats and
 // 16 buckets a thread would take the register budget of two workgroups per
 // CU, which the split grid needs) and take the radix passes on keys.
 template <bool STREAM, bool WIDE_HELD = true, bool VALS = false>
@@ -872,7 +872,7 @@ __device__ __forceinline__ void select_keys(const float* __restrict__ row, int n
 // stage keeps only the register-resident layouts.  SPLIT: the grid may split
 // rows (its segments stage their candidates' scores); otherwise every row
 // is one segment and only indices are staged.  WIDE (split grids): segments
-// of more than 8192 scores also take the one-pass select on floats.
+// of more than 8192 scores also take the value-bucket select on floats.
 template <bool STREAM, bool SPLIT, bool WIDE = false>
 __device__ __forceinline__ void stage1(const TopkArgs& a, TopkShared& sh) {
   const int r = blockIdx.x;
@@ -944,7 +944,7 @@ void topk_split_kernel(const float* __restrict__ logits, int64_t row_stride,
 
 // Stage 1 for split grids whose segments may hold more than 8192 scores
 // (rows longer than 8192 times the grid's segments): such segments take the
-// one-pass select on 16 floats a thread, which leaves room for one
+// value-bucket select on 16 floats a thread, which leaves room for one
 // workgroup per CU, instead of the radix passes (measured on 65K-131K-score
 // rows in 8 segments: a segment's workgroup took 11-25 us in the radix
 // passes).
