@@ -643,9 +643,13 @@ def test_topk_segments_and_workspace_sizes(gpu_lib, ties):
     dense = synth.make_logit_rows(len(lens), width, lens, seed=9, ties=ties)
     rows = len(lens)
     for k in (1, 7, 100, 2048):
-        sizes = [0, gpu_lib.topk_workspace_size(rows, k, 40000),
+        # none; room for 4 segments of 8192 (at k = 2048 the merge of at most
+        # 8192 candidates, which streams rows longer than 4 * 16384 itself);
+        # room for 5; the full split
+        sizes = [0, gpu_lib.topk_workspace_size(rows, k, 32768),
+                 gpu_lib.topk_workspace_size(rows, k, 40000),
                  gpu_lib.topk_workspace_size(rows, k, width)]
-        assert sizes[1] > 0 and sizes[2] > sizes[1]
+        assert 0 < sizes[1] < sizes[2] < sizes[3]
         for nbytes in sizes:
             ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
             _topk_exact(gpu_lib, dense, lens, k, ws, f"segments ties={ties}")
